@@ -1,0 +1,289 @@
+"""Benchmark of the KDA prefill hot path on one MI355X.
+
+One step = one kda_prefill call (every kernel of the path: varlen plan when packed,
+preparation, recurrence) over one batch of synthetic inputs already resident in HBM.
+Default workload: T = 8192 tokens, H = 6 heads, d = 128, BF16 (one GPU's share of a
+96-head model under 16-way head parallelism). Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu-baseline]
+                    [--extra-configs 2,3] [--calib-copy-mib 1024]
+
+Per-kernel durations come from HIP events the library records between its launches on
+the call's stream, accumulated over the timed steps.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+D = 128
+C = 16
+# Algorithmic work per token-head (BF16 I/O): q, k, v, g read (4 x 256 B), beta (2 B),
+# o written (256 B); plus the 128x128 state read and written per (sequence, head).
+BYTES_PER_TOKEN_HEAD_BF16 = 4 * 256 + 2 + 256
+STATE_BYTES_BF16 = 2 * D * D * 2
+# FLOP per token-head: recurrence 6 d^2 + 4 C d (S K_start, S Q_start, U K_end and the
+# two 16x16 products), preparation 2 x 2 C d (R and A_qk as dense 16x16x128 tiles).
+FLOP_REC_PER_TOKEN_HEAD = 6 * D * D + 4 * C * D
+FLOP_PREP_PER_TOKEN_HEAD = 2 * 2 * C * D
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+KERNEL_SOURCES = ["kda_prepare.hip", "kda_recurrence.hip", "kda_device.h", "kda_internal.h"]
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "chunkwise_delta_rule_kda_amd", "csrc")
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(d, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from a committed counter summary, if it matches the current
+    kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"kernel_source_hash:\s*(\w+)", txt)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not b or m.group(1) != kernel_hash():
+        return None
+    return float(b.group(1))
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (one instance)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreate.restype = ctypes.c_int
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.restype = ctypes.c_int
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def make_call(x, device):
+    """Device inputs, outputs and workspace for one configuration (allocated once)."""
+    import torch
+
+    import chunkwise_delta_rule_kda_amd as kda
+    from tests.kda_testlib import to_device
+
+    d = to_device(x, device)
+    o = torch.empty_like(d["v"])
+    st = torch.empty((x.N, x.H, D, D), dtype=d["state_dtype"], device=device)
+    args = kda.make_args(B=x.B, T=x.T, H=x.H, N=x.N, cu_seqlens=d.get("cu_seqlens"))
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(args), dtype=torch.uint8, device=device)
+
+    def call(trace=None):
+        kda.kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                        d.get("cu_seqlens"), scale=x.scale, A_log=d.get("A_log"),
+                        dt_bias=d.get("dt_bias"), lower_bound=d.get("lower_bound"),
+                        l2norm_qk=x.l2norm_qk, beta_is_logit=x.beta_is_logit,
+                        state_dtype=d["state_dtype"], o=o, state_out=st, workspace=ws,
+                        trace_events=trace)
+
+    return call, (o, st)
+
+
+def time_config(x, steps, warmup, device, hip):
+    import torch
+
+    call, _ = make_call(x, device)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = hip.create(3 * steps)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        call(trace=evs[3 * i:3 * i + 3])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    prep = [hip.elapsed_ms(evs[3 * i], evs[3 * i + 1]) for i in range(steps)]
+    rec = [hip.elapsed_ms(evs[3 * i + 1], evs[3 * i + 2]) for i in range(steps)]
+    hip.destroy(evs)
+    return dict(ms_per_step=total_ms / steps, wall_s=t_wall, prep_ms=prep, rec_ms=rec)
+
+
+def cpu_baseline(x, reps=3):
+    """The FP64 oracle on the host, one thread, over the whole workload (reps times)."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import kda_recurrence_fp64
+
+    times = []
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        for _ in range(reps):
+            t = time.perf_counter()
+            kda_recurrence_fp64(x.q, x.k, x.v, x.g, x.beta, **x.oracle_kwargs())
+            times.append(time.perf_counter() - t)
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    med = statistics.median(times)
+    return dict(value=x.tokens() / med, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"whole {x.name} workload ({x.tokens()} tokens x {x.H} heads), "
+                       f"FP64 NumPy token recurrence, median of {reps} runs "
+                       f"({med:.2f} s each), 1 thread")
+
+
+def summarize(x, r):
+    th = x.tokens() * x.H
+    state_b = (2 if x.state0 is not None else 1) * x.N * x.H * D * D * 2
+    prep_us = statistics.mean(r["prep_ms"]) * 1e3
+    rec_us = statistics.mean(r["rec_ms"]) * 1e3
+    tot_us = r["ms_per_step"] * 1e3
+    alg_bytes = th * BYTES_PER_TOKEN_HEAD_BF16 + state_b
+    alg_flop = th * (FLOP_REC_PER_TOKEN_HEAD + FLOP_PREP_PER_TOKEN_HEAD)
+    return dict(
+        us=round(tot_us, 2), tokens_per_s=round(x.tokens() / (tot_us * 1e-6), 1),
+        prepare_us=round(prep_us, 2), recurrence_us=round(rec_us, 2),
+        hbm_frac=round(alg_bytes / (tot_us * 1e-6) / (PEAK_HBM_GBS * 1e9), 5),
+        mfma_frac=round(alg_flop / (tot_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 5),
+        link_ns=round(rec_us * 1e3 / max(1, (x.T + C - 1) // C), 1) if x.cu_seqlens is None
+        else None,
+    )
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--extra-configs", default="2,3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this many MiB first (counter "
+                         "calibration for rocprofv3 --pmc runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the KDA prefill path has no multi-GPU "
+              "component in this build (heads shard across GPUs with no communication).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunkwise_delta_rule_kda_amd as kda
+    import kda_synth
+
+    kda.load_library()
+    device = torch.device("cuda:0")
+    hip = HipEvents()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    x = kda_synth.config(args.config)
+    r = time_config(x, args.steps, args.warmup, device, hip)
+    main_s = summarize(x, r)
+
+    # Dominant kernel: the recurrence (the serial chain). Roofline on its MFMA work.
+    rec_us = statistics.mean(r["rec_ms"]) * 1e3
+    th = x.tokens() * x.H
+    rec_flop = th * FLOP_REC_PER_TOKEN_HEAD
+    achieved = rec_flop / (rec_us * 1e-6) / 1e12
+    workload = f"config{args.config}"
+    roofline = dict(bound="mfma", kernel="kda_recurrence", achieved=round(achieved, 3),
+                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 6),
+                    traffic=traffic_from_profiles("kda_recurrence", workload),
+                    avg_launch_us=round(rec_us, 3))
+
+    per_config = {workload: main_s}
+    for c in [int(c) for c in args.extra_configs.split(",") if c.strip()]:
+        if c == args.config:
+            continue
+        xc = kda_synth.config(c)
+        per_config[f"config{c}"] = summarize(xc, time_config(xc, max(5, args.steps // 5),
+                                                             2, device, hip))
+        del xc
+        torch.cuda.empty_cache()
+    if "config1" in per_config and "config3" in per_config:
+        per_config["head_scaling_t96_over_t6"] = round(
+            per_config["config3"]["us"] / per_config["config1"]["us"], 3)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(x)
+
+    line = {
+        "metric": "KDA prefill tokens/s at T=8192 (H=6 default; H=12/96 under per_config)",
+        "value": round(x.tokens() / (r["ms_per_step"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{workload}: B=1 T={x.T} H={x.H} d=128 chunk=16 "
+                               f"bf16 q,k,v,g,beta; bf16 state", "global_batch": x.B,
+                   "seq_len": x.T, "heads": x.H, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+        "kernel_source_hash": kernel_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,290 @@
+"""Python binding of libkda, the MI355X (gfx950) chunkwise KDA prefill library.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels behind
+the C ABI of ``include/kda.h``. PyTorch supplies device memory and the stream. If the
+library has not been built this module raises on the first call (there is no fallback).
+
+Entry points (same names as the C ABI):
+    kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, ...) -> (o, state_out)
+    kda_prefill_workspace_bytes(...), kda_prefill_check(...), kda_prefill_plan(...)
+    kda_status_string(status), kda_last_error(), kda_debug_check_cu_seqlens(cu, T)
+"""
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "KdaError",
+    "lib_path",
+    "load_library",
+    "kda_prefill",
+    "kda_prefill_args",
+    "kda_prefill_workspace_bytes",
+    "kda_prefill_check",
+    "kda_prefill_plan",
+    "kda_status_string",
+    "kda_last_error",
+    "kda_debug_check_cu_seqlens",
+    "make_args",
+    "KDA_BF16",
+    "KDA_FP32",
+    "KDA_FLAG_L2NORM_QK",
+    "KDA_FLAG_GATE_IN_KERNEL",
+    "KDA_FLAG_BETA_IS_LOGIT",
+    "KDA_WS_RECORD",
+    "STATUS",
+]
+
+KDA_BF16 = 0
+KDA_FP32 = 1
+KDA_FLAG_L2NORM_QK = 1 << 0
+KDA_FLAG_GATE_IN_KERNEL = 1 << 1
+KDA_FLAG_BETA_IS_LOGIT = 1 << 2
+KDA_WS_RECORD = 13824
+HEAD_DIM = 128
+
+STATUS = {
+    0: "KDA_OK",
+    1: "KDA_ERR_NULL",
+    2: "KDA_ERR_SHAPE",
+    3: "KDA_ERR_DTYPE",
+    4: "KDA_ERR_FLAGS",
+    5: "KDA_ERR_BOUND",
+    6: "KDA_ERR_ALIAS",
+    7: "KDA_ERR_WORKSPACE",
+    8: "KDA_ERR_HIP",
+    9: "KDA_ERR_CU_SEQLENS",
+    10: "KDA_ERR_CONFIG",
+}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, detail=""):
+        self.status = status
+        name = STATUS.get(status, str(status))
+        super().__init__(f"{name}: {detail}" if detail else name)
+
+
+class kda_prefill_args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("state_in", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("state_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("B", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("D", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("state_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("lower_bound", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+        ("rows_per_workgroup", ctypes.c_int32),
+        ("trace_events", ctypes.c_void_p),
+        ("n_trace_events", ctypes.c_int32),
+    ]
+
+
+class kda_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("rows_per_workgroup", ctypes.c_int32),
+        ("waves_per_workgroup", ctypes.c_int32),
+        ("recurrence_workgroups", ctypes.c_int64),
+        ("prepare_workgroups", ctypes.c_int64),
+        ("max_chunks", ctypes.c_int64),
+        ("workspace_header_bytes", ctypes.c_size_t),
+    ]
+
+
+def lib_path():
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+
+_LIB = None
+
+
+def load_library():
+    """Load libkda.so (built in-tree by ``__graft_entry__.build()``); raise if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"libkda.so not found at {path}: build it with `python -c \"import "
+            "__graft_entry__ as g; g.build()\"` (there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(kda_prefill_args)
+    lib.kda_prefill.argtypes = [P, ctypes.c_void_p]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill_check.argtypes = [P]
+    lib.kda_prefill_check.restype = ctypes.c_int
+    lib.kda_prefill_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_prefill_workspace_bytes.restype = ctypes.c_int
+    lib.kda_prefill_plan.argtypes = [P, ctypes.c_int32, ctypes.POINTER(kda_plan_info)]
+    lib.kda_prefill_plan.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_debug_check_cu_seqlens.argtypes = [ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_void_p]
+    lib.kda_debug_check_cu_seqlens.restype = ctypes.c_int
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = ctypes.c_int32
+    _LIB = lib
+    return lib
+
+
+def kda_status_string(status):
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def kda_last_error():
+    return load_library().kda_last_error().decode()
+
+
+def _raise_if(status):
+    if status != 0:
+        raise KdaError(status, kda_last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _dtype_code(dt):
+    import torch
+
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_FP32
+    raise KdaError(3, f"unsupported dtype {dt}")
+
+
+def make_args(*, q=None, k=None, v=None, g=None, beta=None, state_in=None, cu_seqlens=None,
+              A_log=None, dt_bias=None, o=None, state_out=None, workspace=None,
+              workspace_bytes=0, B, T, H, N, D=HEAD_DIM, io_dtype=KDA_BF16,
+              state_dtype=KDA_BF16, scale=0.0, lower_bound=0.0, flags=0,
+              rows_per_workgroup=0, trace_events=None):
+    """Fill a kda_prefill_args from raw pointers (ints), tensors or None."""
+    a = kda_prefill_args()
+    a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
+    a.state_in = _ptr(state_in)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.o, a.state_out = _ptr(o), _ptr(state_out)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace_bytes)
+    a.B, a.T, a.H, a.D, a.N = int(B), int(T), int(H), int(D), int(N)
+    a.io_dtype, a.state_dtype = int(io_dtype), int(state_dtype)
+    a.scale = float(scale)
+    a.lower_bound = float(lower_bound)
+    a.flags = int(flags)
+    a.rows_per_workgroup = int(rows_per_workgroup)
+    if trace_events is not None:
+        arr = (ctypes.c_void_p * len(trace_events))(*trace_events)
+        a._trace_keepalive = arr
+        a.trace_events = ctypes.cast(arr, ctypes.c_void_p)
+        a.n_trace_events = len(trace_events)
+    return a
+
+
+def kda_prefill_workspace_bytes(args):
+    n = ctypes.c_size_t(0)
+    _raise_if(load_library().kda_prefill_workspace_bytes(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def kda_prefill_check(args):
+    """Host-only validation; returns the status code (0 = OK)."""
+    return load_library().kda_prefill_check(ctypes.byref(args))
+
+
+def kda_prefill_plan(args, num_cus=256):
+    info = kda_plan_info()
+    _raise_if(load_library().kda_prefill_plan(ctypes.byref(args), int(num_cus),
+                                              ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in kda_plan_info._fields_}
+
+
+def kda_debug_check_cu_seqlens(cu_seqlens, T, stream=None):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    return load_library().kda_debug_check_cu_seqlens(
+        cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(T), s)
+
+
+def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
+                A_log=None, dt_bias=None, lower_bound=None, l2norm_qk=False,
+                beta_is_logit=False, output_final_state=True, state_dtype=None, o=None,
+                state_out=None, workspace=None, rows_per_workgroup=0, stream=None,
+                trace_events=None):
+    """Chunkwise KDA prefill forward on the current (or given) HIP stream.
+
+    q, k, v, g: [B, T, H, 128] bf16 or fp32 CUDA tensors (contiguous); beta [B, T, H].
+    state_in: [N, H, 128, 128] or None. cu_seqlens: int64 [N + 1] (B = 1) or None.
+    A_log / dt_bias / lower_bound: enable the in-kernel gate. Pass state_out=state_in for
+    an in-place state update. Returns (o, state_out or None).
+    """
+    import torch
+
+    lib = load_library()
+    B, T, H, D = q.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    io = _dtype_code(q.dtype)
+    if state_dtype is None:
+        state_dtype = state_in.dtype if state_in is not None else q.dtype
+    st = _dtype_code(state_dtype)
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise KdaError(3, f"{name} must be a contiguous CUDA tensor of {q.dtype}")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int64:
+        raise KdaError(3, "cu_seqlens must be int64")
+    flags = 0
+    if l2norm_qk:
+        flags |= KDA_FLAG_L2NORM_QK
+    if beta_is_logit:
+        flags |= KDA_FLAG_BETA_IS_LOGIT
+    if A_log is not None:
+        flags |= KDA_FLAG_GATE_IN_KERNEL
+        if lower_bound is None:
+            raise KdaError(4, "the in-kernel gate needs lower_bound")
+    if o is None:
+        o = torch.empty_like(v)
+    if state_out is None and output_final_state:
+        state_out = torch.empty((N, H, D, D), dtype=state_dtype, device=q.device)
+    args = make_args(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in,
+                     cu_seqlens=cu_seqlens, A_log=A_log, dt_bias=dt_bias, o=o,
+                     state_out=state_out, B=B, T=T, H=H, N=N, D=D, io_dtype=io,
+                     state_dtype=st, scale=0.0 if scale is None else scale,
+                     lower_bound=0.0 if lower_bound is None else lower_bound,
+                     flags=flags, rows_per_workgroup=rows_per_workgroup,
+                     trace_events=trace_events)
+    need = kda_prefill_workspace_bytes(args)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    args.workspace = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _raise_if(lib.kda_prefill(ctypes.byref(args), stream))
+    return o, state_out

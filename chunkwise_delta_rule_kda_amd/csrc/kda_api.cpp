@@ -1,0 +1,292 @@
+// Host side of libkda: argument validation, launch geometry and the extern "C" entry
+// points declared in include/kda.h. No allocation, no device synchronisation (except in
+// the explicit debug checker), no hidden per-call state.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kda_status fail(kda_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+size_t elem_size(int32_t dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+Range range_of(const void* p, size_t bytes, const char* name) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, p ? lo + bytes : lo, name};
+}
+
+int64_t max_chunks_of(const kda_prefill_args* a) {
+  if (a->cu_seqlens) return (a->T + (kda::kC - 1) * a->N) / kda::kC;
+  return a->N * ((a->T + kda::kC - 1) / kda::kC);
+}
+
+// Shape, dtype, flag and bound checks (no pointers beyond what sizing needs).
+kda_status check_shape(const kda_prefill_args* a) {
+  if (!a) return fail(KDA_ERR_NULL, "args is NULL");
+  if (a->D != KDA_HEAD_DIM) return fail(KDA_ERR_SHAPE, "D=%lld, only 128 is supported", (long long)a->D);
+  if (a->B < 1 || a->T < 0 || a->H < 1 || a->N < 0)
+    return fail(KDA_ERR_SHAPE, "bad B=%lld T=%lld H=%lld N=%lld", (long long)a->B,
+                (long long)a->T, (long long)a->H, (long long)a->N);
+  if (a->H > 65535) return fail(KDA_ERR_SHAPE, "H=%lld exceeds 65535", (long long)a->H);
+  if (a->cu_seqlens) {
+    if (a->B != 1) return fail(KDA_ERR_SHAPE, "packed varlen needs B=1 (got %lld)", (long long)a->B);
+    if (a->N < 1) return fail(KDA_ERR_SHAPE, "packed varlen needs N>=1");
+  } else if (a->N != a->B) {
+    return fail(KDA_ERR_SHAPE, "fixed layout needs N == B (N=%lld, B=%lld)", (long long)a->N,
+                (long long)a->B);
+  }
+  const int64_t mc = max_chunks_of(a);
+  if (mc > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "too many chunks (%lld)", (long long)mc);
+  if (a->N * a->H * 8 > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "N*H too large");
+  if (a->io_dtype != KDA_BF16 && a->io_dtype != KDA_FP32)
+    return fail(KDA_ERR_DTYPE, "io_dtype %d", a->io_dtype);
+  if (a->state_dtype != KDA_BF16 && a->state_dtype != KDA_FP32)
+    return fail(KDA_ERR_DTYPE, "state_dtype %d", a->state_dtype);
+  const uint32_t known = KDA_FLAG_L2NORM_QK | KDA_FLAG_GATE_IN_KERNEL | KDA_FLAG_BETA_IS_LOGIT;
+  if (a->flags & ~known) return fail(KDA_ERR_FLAGS, "unknown flag bits 0x%x", a->flags & ~known);
+  if (a->flags & KDA_FLAG_GATE_IN_KERNEL) {
+    if (!a->A_log || !a->dt_bias)
+      return fail(KDA_ERR_FLAGS, "gate in kernel needs A_log and dt_bias");
+    if (!(a->lower_bound >= -5.0f && a->lower_bound < 0.0f))
+      return fail(KDA_ERR_BOUND, "lower_bound %g outside [-5, 0)", (double)a->lower_bound);
+  }
+  if (!std::isfinite(a->scale) || a->scale < 0.0f)
+    return fail(KDA_ERR_BOUND, "scale %g", (double)a->scale);
+  if (a->rows_per_workgroup != 0 && a->rows_per_workgroup != 16 &&
+      a->rows_per_workgroup != 32 && a->rows_per_workgroup != 64)
+    return fail(KDA_ERR_CONFIG, "rows_per_workgroup %d", a->rows_per_workgroup);
+  return KDA_OK;
+}
+
+size_t header_bytes(const kda_prefill_args* a) {
+  return a->cu_seqlens ? round_up(static_cast<size_t>(a->N + 1) * 8, 256) : 0;
+}
+
+size_t workspace_need(const kda_prefill_args* a) {
+  return header_bytes(a) + static_cast<size_t>(max_chunks_of(a)) * static_cast<size_t>(a->H) *
+                               static_cast<size_t>(kda::kRecord);
+}
+
+int rows_per_wg(const kda_prefill_args* a, int num_cus) {
+  if (a->rows_per_workgroup) return a->rows_per_workgroup;
+  // Smallest slice that keeps the grid within one workgroup per compute unit
+  // (the column-split post's rule, section 3.1), with 16 value rows per wave.
+  const int64_t tasks = a->N * a->H;
+  if (tasks * 8 <= num_cus) return 16;
+  if (tasks * 4 <= num_cus) return 32;
+  return 64;
+}
+
+std::atomic<int> g_cu_count[64];
+
+int cu_count_current(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "shape out of range or inconsistent";
+    case KDA_ERR_DTYPE: return "unsupported dtype";
+    case KDA_ERR_FLAGS: return "unknown flag or missing flag input";
+    case KDA_ERR_BOUND: return "lower_bound or scale out of range";
+    case KDA_ERR_ALIAS: return "output overlaps an input";
+    case KDA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case KDA_ERR_HIP: return "HIP runtime error";
+    case KDA_ERR_CU_SEQLENS: return "cu_seqlens violates its contract";
+    case KDA_ERR_CONFIG: return "unsupported launch configuration";
+  }
+  return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+kda_status kda_prefill_workspace_bytes(const kda_prefill_args* a, size_t* bytes) {
+  g_last_error.clear();
+  const kda_status s = check_shape(a);
+  if (s != KDA_OK) return s;
+  if (!bytes) return fail(KDA_ERR_NULL, "bytes is NULL");
+  *bytes = workspace_need(a);
+  return KDA_OK;
+}
+
+kda_status kda_prefill_check(const kda_prefill_args* a) {
+  g_last_error.clear();
+  kda_status s = check_shape(a);
+  if (s != KDA_OK) return s;
+  const int64_t tokens = a->B * a->T;
+  if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o))
+    return fail(KDA_ERR_NULL, "q, k, v, g, beta and o are required");
+  const size_t es = elem_size(a->io_dtype);
+  const size_t tensor = static_cast<size_t>(tokens) * a->H * KDA_HEAD_DIM * es;
+  const size_t beta_b = static_cast<size_t>(tokens) * a->H * es;
+  const size_t state_b = static_cast<size_t>(a->N) * a->H * KDA_HEAD_DIM * KDA_HEAD_DIM *
+                         elem_size(a->state_dtype);
+  const size_t need = workspace_need(a);
+  if (need > 0) {
+    if (!a->workspace) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (a->workspace_bytes < need)
+      return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", a->workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(a->workspace) % 256)
+      return fail(KDA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  }
+  // Alignment the kernels' vector accesses rely on.
+  const void* vec[] = {a->q, a->k, a->v, a->g, a->o, a->state_in, a->state_out};
+  for (const void* p : vec)
+    if (reinterpret_cast<uintptr_t>(p) % 16)
+      return fail(KDA_ERR_SHAPE, "q, k, v, g, o and state pointers must be 16-byte aligned");
+
+  const Range ins[] = {
+      range_of(a->q, tensor, "q"),          range_of(a->k, tensor, "k"),
+      range_of(a->v, tensor, "v"),          range_of(a->g, tensor, "g"),
+      range_of(a->beta, beta_b, "beta"),    range_of(a->state_in, state_b, "state_in"),
+      range_of(a->cu_seqlens, a->cu_seqlens ? (a->N + 1) * 8 : 0, "cu_seqlens"),
+      range_of(a->A_log, (a->flags & KDA_FLAG_GATE_IN_KERNEL) ? a->H * 4 : 0, "A_log"),
+      range_of(a->dt_bias, (a->flags & KDA_FLAG_GATE_IN_KERNEL) ? a->H * 512 : 0, "dt_bias"),
+  };
+  const Range o = range_of(a->o, tensor, "o");
+  const Range so = range_of(a->state_out, state_b, "state_out");
+  const Range ws = range_of(a->workspace, need, "workspace");
+  const int kStateIn = 5;  // index of state_in in ins[]
+  for (int i = 0; i < static_cast<int>(sizeof ins / sizeof ins[0]); ++i) {
+    const Range& in = ins[i];
+    if (overlap(o, in)) return fail(KDA_ERR_ALIAS, "o overlaps %s", in.name);
+    if (overlap(ws, in)) return fail(KDA_ERR_ALIAS, "workspace overlaps %s", in.name);
+    const bool inplace = i == kStateIn && a->state_out == a->state_in;
+    if (!inplace && overlap(so, in)) return fail(KDA_ERR_ALIAS, "state_out overlaps %s", in.name);
+  }
+  if (overlap(o, so)) return fail(KDA_ERR_ALIAS, "o overlaps state_out");
+  if (overlap(o, ws)) return fail(KDA_ERR_ALIAS, "o overlaps workspace");
+  if (overlap(so, ws)) return fail(KDA_ERR_ALIAS, "state_out overlaps workspace");
+  return KDA_OK;
+}
+
+kda_status kda_prefill_plan(const kda_prefill_args* a, int32_t num_cus, kda_plan_info* out) {
+  g_last_error.clear();
+  const kda_status s = check_shape(a);
+  if (s != KDA_OK) return s;
+  if (!out) return fail(KDA_ERR_NULL, "out is NULL");
+  const int rows = rows_per_wg(a, num_cus > 0 ? num_cus : 256);
+  out->rows_per_workgroup = rows;
+  out->waves_per_workgroup = rows / 16;
+  out->recurrence_workgroups = a->N * a->H * (KDA_HEAD_DIM / rows);
+  out->max_chunks = max_chunks_of(a);
+  out->prepare_workgroups = out->max_chunks * a->H;
+  out->workspace_header_bytes = header_bytes(a);
+  return KDA_OK;
+}
+
+kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
+  kda_status s = kda_prefill_check(a);
+  if (s != KDA_OK) return s;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int rows = rows_per_wg(a, cu_count_current());
+
+  kda::Params p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.g = a->g;
+  p.beta = a->beta;
+  p.state_in = a->state_in;
+  p.cu_seqlens = a->cu_seqlens;
+  p.A_log = a->A_log;
+  p.dt_bias = a->dt_bias;
+  p.o = a->o;
+  p.state_out = a->state_out;
+  p.cu_chunks = a->cu_seqlens ? static_cast<int64_t*>(a->workspace) : nullptr;
+  p.records = static_cast<unsigned char*>(a->workspace) + header_bytes(a);
+  p.B = a->B;
+  p.T = a->T;
+  p.H = a->H;
+  p.N = a->N;
+  p.max_chunks = max_chunks_of(a);
+  p.chunks_per_seq = (a->T + kda::kC - 1) / kda::kC;
+  p.scale = a->scale > 0.0f ? a->scale : 1.0f / std::sqrt(static_cast<float>(KDA_HEAD_DIM));
+  p.lower_bound = a->lower_bound;
+  p.flags = a->flags;
+  p.waves = rows / 16;
+  const bool io_bf16 = a->io_dtype == KDA_BF16;
+  const bool st_bf16 = a->state_dtype == KDA_BF16;
+  const int64_t rec_wgs = a->N * a->H * (KDA_HEAD_DIM / rows);
+  hipEvent_t* ev = nullptr;
+  if (a->trace_events && a->n_trace_events >= 3)
+    ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(a->trace_events));
+
+  hipError_t e = hipSuccess;
+  if (ev) e = hipEventRecord(ev[0], stream);
+  if (e == hipSuccess && a->cu_seqlens) e = kda::launch_plan(p, stream);
+  if (e == hipSuccess && a->T > 0) e = kda::launch_prepare(p, io_bf16, stream);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
+  if (e == hipSuccess) e = kda::launch_recurrence(p, rec_wgs, io_bf16, st_bf16, stream);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+kda_status kda_debug_check_cu_seqlens(const int64_t* cu, int64_t N, int64_t T, void* stream) {
+  g_last_error.clear();
+  if (!cu) return fail(KDA_ERR_NULL, "cu_seqlens is NULL");
+  if (N < 1) return fail(KDA_ERR_SHAPE, "N=%lld", (long long)N);
+  std::vector<int64_t> h(static_cast<size_t>(N + 1));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(h.data(), cu, h.size() * 8, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s", hipGetErrorString(e));
+  if (h[0] != 0) return fail(KDA_ERR_CU_SEQLENS, "cu_seqlens[0]=%lld", (long long)h[0]);
+  for (int64_t i = 0; i < N; ++i)
+    if (h[i + 1] < h[i])
+      return fail(KDA_ERR_CU_SEQLENS, "cu_seqlens decreases at %lld", (long long)i);
+  if (h[N] != T) return fail(KDA_ERR_CU_SEQLENS, "cu_seqlens[N]=%lld != T=%lld", (long long)h[N], (long long)T);
+  return KDA_OK;
+}
+
+}  // extern "C"

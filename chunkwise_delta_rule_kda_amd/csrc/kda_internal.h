@@ -1,0 +1,51 @@
+// Launch parameters shared by the host entry points and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kD = 128;          // head dimension (keys = values = 128)
+constexpr int kC = 16;           // tokens per chunk
+constexpr int kRecord = 13824;   // bytes of one prepared (chunk, head) record
+constexpr int kOffKn = 0;        // bf16 [4][64][8]
+constexpr int kOffQt = 4096;     // bf16 [4][64][8]
+constexpr int kOffKeT = 8192;    // bf16 [8][64][4]
+constexpr int kOffD = 12288;     // fp32 [128]
+constexpr int kOffMb = 12800;    // bf16 [64][4]
+constexpr int kOffAqk = 13312;   // bf16 [64][4]
+
+constexpr uint32_t kFlagL2 = 1u << 0;
+constexpr uint32_t kFlagGate = 1u << 1;
+constexpr uint32_t kFlagBetaLogit = 1u << 2;
+
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const void* state_in;
+  const int64_t* cu_seqlens;  // null: fixed layout
+  const float* A_log;
+  const float* dt_bias;
+  void* o;
+  void* state_out;
+  int64_t* cu_chunks;         // workspace header (varlen only)
+  unsigned char* records;     // workspace records
+  int64_t B, T, H, N;
+  int64_t max_chunks;         // prepare grid width (upper bound on chunks)
+  int64_t chunks_per_seq;     // fixed layout: ceil(T / 16)
+  float scale;
+  float lower_bound;
+  uint32_t flags;
+  int32_t waves;              // recurrence waves per workgroup (16 value rows each)
+};
+
+hipError_t launch_plan(const Params& p, hipStream_t stream);
+hipError_t launch_prepare(const Params& p, bool io_bf16, hipStream_t stream);
+hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16,
+                             bool state_bf16, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,198 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) chunkwise Kimi Delta Attention prefill library.
+ *
+ * The operation (one call = the whole prefill forward of every sequence and head):
+ * for each sequence n and head h, starting from the state S (values x keys, 128 x 128)
+ * given in state_in[n, h] (or zeros), every token t updates
+ *
+ *     S <- S Diag(exp g_t) ;  S <- S + beta_t (v_t - S k_t) k_t^T ;  o_t = scale * S q_t
+ *
+ * and the final S is written to state_out[n, h]. This is the token form of the chunk
+ * equations of the "FlashKDA column split" post (section 1, "FlashKDA in two kernels"):
+ * the library evaluates it chunk by chunk (16 tokens) with a chunk-parallel preparation
+ * kernel and a serial recurrence kernel whose 128 value rows are split across compute
+ * units (section 3.1 of the same post: value rows never interact).
+ *
+ * The calling contract follows the "flashinfer.kda_prefill" API page (sections
+ * "Optimized Blackwell prefill subset", "SM120a prefill subset" and "State and graph
+ * semantics"): contiguous [B, T, H, 128] q, k, v, g; [B, T, H] beta; one shared head
+ * count; head dimension 128; packed varlen through int64 cu_seqlens with B = 1;
+ * state layout [N, H, V, K]; in-place state update allowed; optional in-kernel q/k L2
+ * normalisation, beta from logits and the lower-bounded gate with lower_bound in [-5, 0).
+ *
+ * Ownership: the caller allocates every buffer (inputs, outputs, workspace). The library
+ * allocates nothing, keeps no per-call caches and holds no global state besides a
+ * per-device compute-unit count. All pointers in kda_prefill_args are device pointers
+ * unless stated otherwise.
+ *
+ * Errors: every entry point returns a kda_status; nothing aborts or throws across the
+ * ABI. Host-checkable violations are rejected before any launch. Device-side contract
+ * violations (non-monotone cu_seqlens, cu_seqlens[0] != 0, cu_seqlens[N] != T, a
+ * precomputed g outside [-5, 0]) are undefined behaviour, as on the flashinfer page;
+ * kda_debug_check_cu_seqlens is the explicit (synchronising) checker for tests.
+ *
+ * Indexing is 64-bit throughout: there is no 2^31 extent limit.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+#define KDA_HEAD_DIM 128 /* d_k = d_v = 128 */
+#define KDA_CHUNK 16     /* tokens per chunk */
+
+typedef enum kda_dtype {
+  KDA_BF16 = 0, /* bfloat16, round-to-nearest-even on output */
+  KDA_FP32 = 1  /* IEEE float32 */
+} kda_dtype;
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,       /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 2,      /* B, T, H, N or D out of range, or inconsistent */
+  KDA_ERR_DTYPE = 3,      /* io_dtype or state_dtype not a kda_dtype */
+  KDA_ERR_FLAGS = 4,      /* unknown flag bit, or a flag's companion input missing */
+  KDA_ERR_BOUND = 5,      /* lower_bound outside [-5, 0), or scale not finite */
+  KDA_ERR_ALIAS = 6,      /* an output overlaps an input (state_out == state_in is allowed) */
+  KDA_ERR_WORKSPACE = 7,  /* workspace NULL, too small or not 256-byte aligned */
+  KDA_ERR_HIP = 8,        /* a HIP runtime call or kernel launch failed */
+  KDA_ERR_CU_SEQLENS = 9, /* kda_debug_check_cu_seqlens found a contract violation */
+  KDA_ERR_CONFIG = 10     /* rows_per_workgroup not one of 0, 16, 32, 64 */
+} kda_status;
+
+enum {
+  /* q <- q / sqrt(sum q^2 + 1e-6), same for k, per (token, head), before anything else */
+  KDA_FLAG_L2NORM_QK = 1u << 0,
+  /* g <- lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h, c])); needs A_log,
+     dt_bias and lower_bound in [-5, 0) */
+  KDA_FLAG_GATE_IN_KERNEL = 1u << 1,
+  /* beta <- sigmoid(beta) */
+  KDA_FLAG_BETA_IS_LOGIT = 1u << 2
+};
+
+typedef struct kda_prefill_args {
+  /* Inputs (device, contiguous, read only).
+     q, k, v, g: [B, T, H, 128] of io_dtype. beta: [B, T, H] of io_dtype.
+     Without KDA_FLAG_GATE_IN_KERNEL, g is the per-channel natural-log decay and must
+     lie in [-5, 0] (16 tokens of it must keep exp(+-sum) finite, the K3 decay page's
+     range argument); with it, g is the raw gate input. */
+  const void *q, *k, *v, *g, *beta;
+  /* [N, H, 128 (values), 128 (keys)] of state_dtype, or NULL for a zero initial state. */
+  const void *state_in;
+  /* int64 [N + 1] packed-varlen offsets (B must be 1, T = total tokens), or NULL for the
+     fixed layout (N = B sequences of T tokens). Contract: cu[0] = 0, non-decreasing,
+     cu[N] = T. Zero-length sequences are allowed and pass their state through. */
+  const int64_t *cu_seqlens;
+  /* FP32 [H] and [H, 128]; read only with KDA_FLAG_GATE_IN_KERNEL. */
+  const float *A_log, *dt_bias;
+
+  /* Outputs (device). o: [B, T, H, 128] of io_dtype, must not overlap any input.
+     state_out: [N, H, 128, 128] of state_dtype, or NULL (no final state written);
+     it may be exactly state_in (in-place update) but must not partially overlap it. */
+  void *o;
+  void *state_out;
+
+  /* Caller-owned scratch of at least kda_prefill_workspace_bytes() bytes, 256-byte
+     aligned. After a successful call it holds the prepared per-chunk records whose
+     layout is given below. */
+  void *workspace;
+  size_t workspace_bytes;
+
+  int64_t B, T, H, D, N; /* D must be 128; N = number of sequences */
+  int32_t io_dtype;      /* kda_dtype of q, k, v, g, beta and o */
+  int32_t state_dtype;   /* kda_dtype of state_in and state_out */
+  float scale;           /* output scale s; 0 selects 1/sqrt(128) */
+  float lower_bound;     /* gate lower bound, in [-5, 0); used with the gate flag */
+  uint32_t flags;        /* KDA_FLAG_* */
+
+  /* Launch geometry: value rows handled by one workgroup of the recurrence (each
+     wave owns 16 rows). 0 = automatic (fill the compute units); 16/32/64 force it.
+     Results are bitwise identical for every choice. */
+  int32_t rows_per_workgroup;
+
+  /* Optional timing hooks (host array of hipEvent_t handles, or NULL). When
+     n_trace_events >= 3, the library records trace_events[0] before the first kernel,
+     trace_events[1] between the preparation and recurrence kernels and
+     trace_events[2] after the recurrence kernel, all on the call's stream. */
+  void *const *trace_events;
+  int32_t n_trace_events;
+} kda_prefill_args;
+
+/*
+ * Workspace layout (bytes, from the workspace base):
+ *   [0, KDA_WS_HEADER)            int64 cu_chunks[N + 1] (varlen only): exclusive prefix
+ *                                 of ceil(len_n / 16) (the flashinfer page's compact
+ *                                 chunk prefix, section "Packed scheduling").
+ *   [KDA_WS_HEADER, ...)          one KDA_WS_RECORD-byte record per (chunk c, head h)
+ *                                 at index c * H + h, where c counts chunks over all
+ *                                 sequences in order.
+ * KDA_WS_HEADER = round_up((N + 1) * 8, 256).
+ *
+ * A record holds, for the chunk's 16 tokens (pad tokens of a short last chunk behave as
+ * k = q = v = 0, g = 0, beta = 0), with the page's K_start, Q_start, K_end, D_{0:15},
+ * A_kk = (I + R)^{-1} and A_qk and B = Diag(beta):
+ *   Mb  = A_kk B                              (16 x 16)
+ *   Kn  = -Mb K_start^T                       (16 tokens x 128 keys)
+ *   Qt  = s Q_start^T + A_qk Kn               (16 tokens x 128 keys)
+ * so that a chunk entering with state S gives U^T = Mb V^T + Kn S^T,
+ * O^T = Qt S^T + A_qk Mb V^T and S_next^T = D_{0:15} S^T + K_end^T U^T.
+ * Offsets inside a record (tok m, lane L = 16 * grp + m, key index
+ * kappa(kb, grp, e) = 32 kb + 16 (e / 4) + 4 grp + (e % 4)):
+ *   0      bf16 Kn [kb 4][L 64][e 8]  = Kn[m][kappa(kb, grp, e)]
+ *   4096   bf16 Qt [kb 4][L 64][e 8]  = Qt[m][kappa(kb, grp, e)]
+ *   8192   bf16 KeT[b 8][L 64][j 4]   = K_end[4 grp + j][16 b + m]
+ *   12288  fp32 D  [128]              = D_{0:15}[key]
+ *   12800  bf16 Mb [L 64][j 4]        = Mb[m][4 grp + j]
+ *   13312  bf16 Aqk[L 64][j 4]        = A_qk[m][4 grp + j]
+ */
+#define KDA_WS_RECORD 13824
+
+/* Host only; no HIP call. Validates shapes, dtypes, flags and bound, and stores the
+   workspace size the call needs in *bytes. */
+kda_status kda_prefill_workspace_bytes(const kda_prefill_args *a, size_t *bytes);
+
+/* Host only; no HIP call. Every check kda_prefill does before launching (pointers,
+   shapes, dtypes, flags, bound, aliasing, workspace size and alignment). */
+kda_status kda_prefill_check(const kda_prefill_args *a);
+
+/* Enqueue the whole prefill on `stream` (a hipStream_t; NULL = default stream).
+   Asynchronous: no device synchronisation, no device-to-host read of cu_seqlens.
+   Launch geometry uses the upper bound (T + 15 N) / 16 on the total chunk count. */
+kda_status kda_prefill(const kda_prefill_args *a, void *stream);
+
+/* Static description of a status code. */
+const char *kda_status_string(kda_status s);
+
+/* Detail of the last failure on the calling thread (empty string if none). */
+const char *kda_last_error(void);
+
+/* Tests only: copies cu_seqlens to the host (synchronising `stream`) and checks
+   cu[0] = 0, non-decreasing entries and cu[N] = T. Returns KDA_OK or KDA_ERR_CU_SEQLENS. */
+kda_status kda_debug_check_cu_seqlens(const int64_t *cu_seqlens, int64_t N, int64_t T,
+                                      void *stream);
+
+/* Launch geometry the call would use (host only): recurrence rows per workgroup,
+   workgroup count of each kernel, and the upper bound on the chunk count. */
+typedef struct kda_plan_info {
+  int32_t rows_per_workgroup;
+  int32_t waves_per_workgroup;
+  int64_t recurrence_workgroups;
+  int64_t prepare_workgroups;
+  int64_t max_chunks;
+  size_t workspace_header_bytes;
+} kda_plan_info;
+kda_status kda_prefill_plan(const kda_prefill_args *a, int32_t num_cus, kda_plan_info *out);
+
+int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -175,9 +175,11 @@ def config(i, *, T=None, H=None, B=None, lengths=None, seed=None, dtype=None):
     if i == 4:
         if lengths is None:
             lengths = varlen_lengths(rng, s["N"], s["lmin"], s["lmax"])
-        return _raw_gate_family(f"config4", rng, lengths, H or s["H"], dt, -5.0)
+        return _raw_gate_family("config4", rng, lengths, s["H"] if H is None else H, dt,
+                                -5.0)
     state_sd = 0.02 if i == 2 else None
-    return _normal_family(f"config{i}", rng, B or s["B"], T or s["T"], H or s["H"], dt,
+    pick = lambda v, key: s[key] if v is None else v
+    return _normal_family(f"config{i}", rng, pick(B, "B"), pick(T, "T"), pick(H, "H"), dt,
                           state_sd)
 
 

@@ -1,0 +1,151 @@
+"""The C-ABI library loads, exports every declared symbol, and its host-side validation
+rejects what the contract forbids (CPU only: no HIP call is made; pointers are fake)."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+import chunkwise_delta_rule_kda_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kda.lib_path()),
+                                reason="libkda.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["kda_prefill", "kda_prefill_workspace_bytes", "kda_prefill_check",
+              "kda_status_string", "kda_last_error", "kda_debug_check_cu_seqlens",
+              "kda_prefill_plan", "kda_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    lib = kda.load_library()
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_abi_version_and_status_strings():
+    lib = kda.load_library()
+    assert lib.kda_abi_version() == 1
+    for code in range(11):
+        assert kda.kda_status_string(code) and kda.kda_status_string(code) != "unknown status"
+    assert kda.kda_status_string(99) == "unknown status"
+
+
+MB = 1 << 20
+
+
+def fake(B=1, T=64, H=2, N=None, varlen=False, io=kda.KDA_BF16, st=kda.KDA_BF16, **kw):
+    """Args with fake, disjoint, aligned device addresses (never dereferenced)."""
+    base = 0x7F0000000000
+    slot = lambda i: base + i * 256 * MB
+    N = (B if not varlen else 3) if N is None else N
+    d = dict(q=slot(0), k=slot(1), v=slot(2), g=slot(3), beta=slot(4), state_in=slot(5),
+             o=slot(6), state_out=slot(7), workspace=slot(8), workspace_bytes=200 * MB,
+             B=B, T=T, H=H, N=N, io_dtype=io, state_dtype=st)
+    if varlen:
+        d["cu_seqlens"] = slot(9)
+    d.update(kw)
+    return kda.make_args(**d)
+
+
+def status(a):
+    return kda.kda_prefill_check(a)
+
+
+def test_valid_args_pass():
+    assert status(fake()) == 0
+    assert status(fake(varlen=True)) == 0
+    assert status(fake(io=kda.KDA_FP32, st=kda.KDA_FP32)) == 0
+    assert status(fake(state_in=None)) == 0          # zero initial state
+    assert status(fake(state_out=None)) == 0         # no final state
+    assert status(fake(state_out=0x7F0000000000 + 5 * 256 * MB)) == 0  # in place
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "g", "beta", "o"])
+def test_null_required_pointer(field):
+    assert status(fake(**{field: None})) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), 2), (dict(H=0), 2), (dict(T=-1), 2), (dict(B=2, N=3), 2),
+    (dict(io_dtype=7), 3), (dict(state_dtype=-1), 3),
+    (dict(flags=1 << 5), 4), (dict(rows_per_workgroup=24), 10),
+    (dict(scale=float("nan")), 5),
+])
+def test_shape_dtype_flag_rejections(kw, code):
+    assert status(fake(**kw)) == code
+
+
+def test_varlen_needs_batch_one():
+    assert status(fake(B=2, varlen=True)) == 2
+
+
+def test_gate_needs_params_and_bound():
+    G = kda.KDA_FLAG_GATE_IN_KERNEL
+    p = dict(A_log=0x7F0000000000 + 10 * 256 * MB, dt_bias=0x7F0000000000 + 11 * 256 * MB)
+    assert status(fake(flags=G, lower_bound=-5.0)) == 4          # no A_log / dt_bias
+    assert status(fake(flags=G, lower_bound=-5.0, **p)) == 0
+    assert status(fake(flags=G, lower_bound=-0.1, **p)) == 0
+    # The flashinfer page's accepted range is [-5, 0): the cliff near -5.4585 is outside.
+    for lb in (-5.4585, -5.0001, 0.0, 0.5, float("nan")):
+        assert status(fake(flags=G, lower_bound=lb, **p)) == 5, lb
+
+
+def test_aliasing_rejected():
+    base = 0x7F0000000000
+    assert status(fake(o=base + 1 * 256 * MB)) == 6                 # o == k
+    assert status(fake(o=base + 2 * 256 * MB + 4096)) == 6          # o inside v
+    assert status(fake(state_out=base + 5 * 256 * MB + 64)) == 6    # partial overlap
+    assert status(fake(state_out=base + 0 * 256 * MB)) == 6         # state_out == q
+    assert status(fake(workspace=base + 4 * 256 * MB)) == 6         # workspace == beta
+    assert status(fake(state_out=base + 6 * 256 * MB)) == 6         # state_out == o
+
+
+def test_workspace_checks():
+    a = fake(T=100, H=3)
+    need = kda.kda_prefill_workspace_bytes(a)
+    assert need == 7 * 3 * kda.KDA_WS_RECORD  # ceil(100/16) = 7 chunks, 3 heads
+    assert status(fake(T=100, H=3, workspace_bytes=need)) == 0
+    assert status(fake(T=100, H=3, workspace_bytes=need - 1)) == 7
+    assert status(fake(T=100, H=3, workspace=None)) == 7
+    assert status(fake(T=100, H=3, workspace=0x7F0000000000 + 8 * 256 * MB + 128)) == 7
+    # varlen: (T + 15 N) / 16 chunk records plus the 256-byte-rounded cu_chunks header
+    v = fake(T=100, H=3, N=5, varlen=True)
+    assert kda.kda_prefill_workspace_bytes(v) == 256 + ((100 + 15 * 5) // 16) * 3 * kda.KDA_WS_RECORD
+
+
+def test_misaligned_vector_pointer_rejected():
+    assert status(fake(q=0x7F0000000000 + 8)) == 2
+
+
+def test_plan_follows_the_slice_rule():
+    # Smallest slice keeping N*H*(128/rows) within the compute units, 16 rows per wave.
+    assert kda.kda_prefill_plan(fake(H=6), 256)["rows_per_workgroup"] == 16
+    assert kda.kda_prefill_plan(fake(H=12), 256)["rows_per_workgroup"] == 16
+    assert kda.kda_prefill_plan(fake(H=48), 256)["rows_per_workgroup"] == 32
+    p = kda.kda_prefill_plan(fake(H=96, T=8192), 256)
+    assert p["rows_per_workgroup"] == 64 and p["recurrence_workgroups"] == 192
+    assert p["prepare_workgroups"] == 512 * 96
+    assert kda.kda_prefill_plan(fake(H=6, rows_per_workgroup=64), 256)["recurrence_workgroups"] == 12
+
+
+def test_last_error_explains_rejection():
+    assert status(fake(D=64)) == 2
+    assert "128" in kda.kda_last_error()
