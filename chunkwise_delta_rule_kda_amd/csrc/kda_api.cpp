@@ -86,7 +86,8 @@ kda_status check_shape(const kda_prefill_args* a) {
   if (!std::isfinite(a->scale) || a->scale < 0.0f)
     return fail(KDA_ERR_BOUND, "scale %g", (double)a->scale);
   if (a->rows_per_workgroup != 0 && a->rows_per_workgroup != 16 &&
-      a->rows_per_workgroup != 32 && a->rows_per_workgroup != 64)
+      a->rows_per_workgroup != 32 && a->rows_per_workgroup != 64 &&
+      a->rows_per_workgroup != 128)
     return fail(KDA_ERR_CONFIG, "rows_per_workgroup %d", a->rows_per_workgroup);
   return KDA_OK;
 }

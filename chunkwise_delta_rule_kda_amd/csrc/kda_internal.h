@@ -45,6 +45,7 @@ struct Params {
 
 hipError_t launch_plan(const Params& p, hipStream_t stream);
 hipError_t launch_prepare(const Params& p, bool io_bf16, hipStream_t stream);
+int recurrence_loader_waves(int compute_waves);
 hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16,
                              bool state_bf16, hipStream_t stream);
 

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
     valid = min<int64_t>(kC, p.T - kC * lc);
   }
   if (tok0 < 0) valid = 0;
-  unsigned char* rec = p.records + (gc * H + h) * (int64_t)kRecord;
+  unsigned char* rec = p.records + (h * p.max_chunks + gc) * (int64_t)kRecord;
 
   // ---- load the chunk's rows and apply the optional transforms -------------------
   const int r = tid >> 4;         // token of the chunk

@@ -63,7 +63,7 @@ typedef enum kda_status {
   KDA_ERR_WORKSPACE = 7,  /* workspace NULL, too small or not 256-byte aligned */
   KDA_ERR_HIP = 8,        /* a HIP runtime call or kernel launch failed */
   KDA_ERR_CU_SEQLENS = 9, /* kda_debug_check_cu_seqlens found a contract violation */
-  KDA_ERR_CONFIG = 10     /* rows_per_workgroup not one of 0, 16, 32, 64 */
+  KDA_ERR_CONFIG = 10     /* rows_per_workgroup not one of 0, 16, 32, 64, 128 */
 } kda_status;
 
 enum {
@@ -112,7 +112,7 @@ typedef struct kda_prefill_args {
   uint32_t flags;        /* KDA_FLAG_* */
 
   /* Launch geometry: value rows handled by one workgroup of the recurrence (each
-     wave owns 16 rows). 0 = automatic (fill the compute units); 16/32/64 force it.
+     wave owns 16 rows). 0 = automatic (fill the compute units); 16/32/64/128 force it.
      Results are bitwise identical for every choice. */
   int32_t rows_per_workgroup;
 
@@ -130,8 +130,10 @@ typedef struct kda_prefill_args {
  *                                 of ceil(len_n / 16) (the flashinfer page's compact
  *                                 chunk prefix, section "Packed scheduling").
  *   [KDA_WS_HEADER, ...)          one KDA_WS_RECORD-byte record per (chunk c, head h)
- *                                 at index c * H + h, where c counts chunks over all
- *                                 sequences in order.
+ *                                 at index h * max_chunks + c, where c counts chunks
+ *                                 over all sequences in order and max_chunks is the
+ *                                 plan's bound (kda_prefill_plan): N * ceil(T / 16)
+ *                                 for the fixed layout, (T + 15 N) / 16 for varlen.
  * KDA_WS_HEADER = round_up((N + 1) * 8, 256).
  *
  * A record holds, for the chunk's 16 tokens (pad tokens of a short last chunk behave as

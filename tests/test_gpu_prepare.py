@@ -80,6 +80,8 @@ def run_and_check(x, chunks_to_check=None, tols=TOLS):
     torch.cuda.synchronize()
     wsn = ws.cpu().numpy()
     header = 0 if x.cu_seqlens is None else ((x.N + 1) * 8 + 255) // 256 * 256
+    max_chunks = (x.N * ((x.T + 15) // 16) if x.cu_seqlens is None
+                  else (x.T + 15 * x.N) // 16)
     # Oracle-side inputs after the in-kernel transforms (FP64).
     q64, k64, g64, b64 = (np.asarray(a, np.float64) for a in (x.q, x.k, x.g, x.beta))
     if x.l2norm_qk:
@@ -99,7 +101,7 @@ def run_and_check(x, chunks_to_check=None, tols=TOLS):
             sl = slice(c0, min(c0 + 16, int(b)))
             if chunks_to_check is None or gc in chunks_to_check:
                 for h in range(x.H):
-                    off = header + (gc * x.H + h) * REC
+                    off = header + (h * max_chunks + gc) * REC
                     got = decode(wsn[off:off + REC])
                     ref = expected(q64[sl, h], k64[sl, h], g64[sl, h], b64[sl, h], x.scale)
                     for n in TOLS:
