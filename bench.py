@@ -148,8 +148,9 @@ def time_config(x, steps, warmup, device, hip):
     return dict(ms_per_step=total_ms / steps, wall_s=t_wall, prep_ms=prep, rec_ms=rec)
 
 
-def cpu_baseline(x, reps=3):
-    """The FP64 oracle on the host, one thread, over the whole workload (reps times)."""
+def cpu_baseline(x, budget_s=10.0, max_reps=30):
+    """The FP64 oracle on the host, one thread, over the whole workload: repeated until
+    about budget_s seconds of CPU work (at least one run), median reported."""
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
@@ -161,7 +162,7 @@ def cpu_baseline(x, reps=3):
     try:
         if ctx:
             ctx.__enter__()
-        for _ in range(reps):
+        while not times or (sum(times) < budget_s and len(times) < max_reps):
             t = time.perf_counter()
             kda_recurrence_fp64(x.q, x.k, x.v, x.g, x.beta, **x.oracle_kwargs())
             times.append(time.perf_counter() - t)
@@ -169,10 +170,14 @@ def cpu_baseline(x, reps=3):
         if ctx:
             ctx.__exit__(None, None, None)
     med = statistics.median(times)
-    return dict(value=x.tokens() / med, unit="tokens/s", cores=1, kind="oracle",
+    return dict(value=round(x.tokens() / med, 1), unit="tokens/s", cores=1, kind="oracle",
                 sample=f"whole {x.name} workload ({x.tokens()} tokens x {x.H} heads), "
-                       f"FP64 NumPy token recurrence, median of {reps} runs "
-                       f"({med:.2f} s each), 1 thread")
+                       f"FP64 NumPy token recurrence, median of {len(times)} runs "
+                       f"({med:.2f} s each, {sum(times):.1f} s total), 1 thread")
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def summarize(x, r):
@@ -233,6 +238,7 @@ def main():
     x = kda_synth.config(args.config)
     r = time_config(x, args.steps, args.warmup, device, hip)
     main_s = summarize(x, r)
+    progress(f"config{args.config}: {main_s}")
 
     # Dominant kernel: the recurrence (the serial chain). Roofline on its MFMA work.
     rec_us = statistics.mean(r["rec_ms"]) * 1e3
@@ -253,6 +259,7 @@ def main():
         xc = kda_synth.config(c)
         per_config[f"config{c}"] = summarize(xc, time_config(xc, max(5, args.steps // 5),
                                                              2, device, hip))
+        progress(f"config{c}: {per_config[f'config{c}']}")
         del xc
         torch.cuda.empty_cache()
     if "config1" in per_config and "config3" in per_config:
@@ -260,6 +267,8 @@ def main():
             per_config["config3"]["us"] / per_config["config1"]["us"], 3)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(x)
+    if cpu:
+        progress(f"cpu_baseline: {cpu['value']} tokens/s")
 
     line = {
         "metric": "KDA prefill tokens/s at T=8192 (H=6 default; H=12/96 under per_config)",
