@@ -92,6 +92,7 @@ class kda_prefill_args(ctypes.Structure):
         ("lower_bound", ctypes.c_float),
         ("flags", ctypes.c_uint32),
         ("rows_per_workgroup", ctypes.c_int32),
+        ("segment_chunks", ctypes.c_int32),
         ("trace_events", ctypes.c_void_p),
         ("n_trace_events", ctypes.c_int32),
     ]
@@ -105,6 +106,12 @@ class kda_plan_info(ctypes.Structure):
         ("prepare_workgroups", ctypes.c_int64),
         ("max_chunks", ctypes.c_int64),
         ("workspace_header_bytes", ctypes.c_size_t),
+        ("segment_chunks", ctypes.c_int64),
+        ("segments_per_head_bound", ctypes.c_int64),
+        ("combine_workgroups", ctypes.c_int64),
+        ("scan_c_workgroups", ctypes.c_int64),
+        ("scan_state_offset", ctypes.c_size_t),
+        ("scan_transition_offset", ctypes.c_size_t),
     ]
 
 
@@ -183,7 +190,7 @@ def make_args(*, q=None, k=None, v=None, g=None, beta=None, state_in=None, cu_se
               A_log=None, dt_bias=None, o=None, state_out=None, workspace=None,
               workspace_bytes=0, B, T, H, N, D=HEAD_DIM, io_dtype=KDA_BF16,
               state_dtype=KDA_BF16, scale=0.0, lower_bound=0.0, flags=0,
-              rows_per_workgroup=0, trace_events=None):
+              rows_per_workgroup=0, segment_chunks=0, trace_events=None):
     """Fill a kda_prefill_args from raw pointers (ints), tensors or None."""
     a = kda_prefill_args()
     a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
@@ -199,6 +206,7 @@ def make_args(*, q=None, k=None, v=None, g=None, beta=None, state_in=None, cu_se
     a.lower_bound = float(lower_bound)
     a.flags = int(flags)
     a.rows_per_workgroup = int(rows_per_workgroup)
+    a.segment_chunks = int(segment_chunks)
     if trace_events is not None:
         arr = (ctypes.c_void_p * len(trace_events))(*trace_events)
         a._trace_keepalive = arr
@@ -236,14 +244,15 @@ def kda_debug_check_cu_seqlens(cu_seqlens, T, stream=None):
 def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                 A_log=None, dt_bias=None, lower_bound=None, l2norm_qk=False,
                 beta_is_logit=False, output_final_state=True, state_dtype=None, o=None,
-                state_out=None, workspace=None, rows_per_workgroup=0, stream=None,
-                trace_events=None):
+                state_out=None, workspace=None, rows_per_workgroup=0, segment_chunks=0,
+                stream=None, trace_events=None):
     """Chunkwise KDA prefill forward on the current (or given) HIP stream.
 
     q, k, v, g: [B, T, H, 128] bf16 or fp32 CUDA tensors (contiguous); beta [B, T, H].
     state_in: [N, H, 128, 128] or None. cu_seqlens: int64 [N + 1] (B = 1) or None.
     A_log / dt_bias / lower_bound: enable the in-kernel gate. Pass state_out=state_in for
-    an in-place state update. Returns (o, state_out or None).
+    an in-place state update. segment_chunks: 0 automatic, negative serial, positive
+    the time-segment length in chunks. Returns (o, state_out or None).
     """
     import torch
 
@@ -278,7 +287,7 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                      state_dtype=st, scale=0.0 if scale is None else scale,
                      lower_bound=0.0 if lower_bound is None else lower_bound,
                      flags=flags, rows_per_workgroup=rows_per_workgroup,
-                     trace_events=trace_events)
+                     segment_chunks=segment_chunks, trace_events=trace_events)
     need = kda_prefill_workspace_bytes(args)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

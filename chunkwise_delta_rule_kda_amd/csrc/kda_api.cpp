@@ -86,19 +86,11 @@ kda_status check_shape(const kda_prefill_args* a) {
   if (!std::isfinite(a->scale) || a->scale < 0.0f)
     return fail(KDA_ERR_BOUND, "scale %g", (double)a->scale);
   if (a->rows_per_workgroup != 0 && a->rows_per_workgroup != 16 &&
-      a->rows_per_workgroup != 32 && a->rows_per_workgroup != 64 &&
-      a->rows_per_workgroup != 128)
+      a->rows_per_workgroup != 32 && a->rows_per_workgroup != 64)
     return fail(KDA_ERR_CONFIG, "rows_per_workgroup %d", a->rows_per_workgroup);
+  if (a->segment_chunks > (1 << 24))
+    return fail(KDA_ERR_CONFIG, "segment_chunks %d", a->segment_chunks);
   return KDA_OK;
-}
-
-size_t header_bytes(const kda_prefill_args* a) {
-  return a->cu_seqlens ? round_up(static_cast<size_t>(a->N + 1) * 8, 256) : 0;
-}
-
-size_t workspace_need(const kda_prefill_args* a) {
-  return header_bytes(a) + static_cast<size_t>(max_chunks_of(a)) * static_cast<size_t>(a->H) *
-                               static_cast<size_t>(kda::kRecord);
 }
 
 int rows_per_wg(const kda_prefill_args* a, int num_cus) {
@@ -109,6 +101,83 @@ int rows_per_wg(const kda_prefill_args* a, int num_cus) {
   if (tasks * 8 <= num_cus) return 16;
   if (tasks * 4 <= num_cus) return 32;
   return 64;
+}
+
+// Compute units the automatic segment rule is tuned for (MI355X). The rule must not
+// depend on the device so that the workspace size is a pure function of the arguments.
+constexpr int64_t kScanTargetCUs = 256;
+
+// Launch geometry and workspace layout of one call.
+struct Plan {
+  int64_t max_chunks = 0;
+  int64_t seg_len = 0;       // chunks per segment; 0 = serial recurrence
+  int64_t segs_per_seq = 0;  // fixed layout
+  int64_t seg_stride = 0;    // scan slots per head
+  size_t header = 0;         // cu_chunks [N + 1] and cu_segs [N + 1] (varlen)
+  size_t records = 0;        // offset of the records
+  size_t scan_s = 0;         // offset of the FP32 scan states
+  size_t scan_phi = 0;       // offset of the BF16 transitions
+  size_t total = 0;
+};
+
+Plan make_plan(const kda_prefill_args* a) {
+  Plan pl;
+  pl.max_chunks = max_chunks_of(a);
+  const int64_t per_seq = a->cu_seqlens ? (a->N > 0 ? pl.max_chunks / a->N : 0)
+                                        : (a->T + kda::kC - 1) / kda::kC;
+  int64_t L = 0;
+  if (a->segment_chunks > 0) {
+    L = a->segment_chunks;
+  } else if (a->segment_chunks == 0) {
+    // Time segments pay off when few (sequence, head) pairs leave compute units idle:
+    // launch A has about 4 P - 6 workgroups of 64 rows per pair for P segments; aim
+    // for one per compute unit, with segments of at least 16 chunks.
+    const int64_t pairs = a->N * a->H;
+    if (pairs > 0 && pairs * 8 <= kScanTargetCUs) {
+      const int64_t P = (kScanTargetCUs / pairs + 6) / 4;
+      if (P >= 2) {
+        L = (per_seq + P - 1) / P;
+        if (L < 16) L = 16;
+      }
+    }
+  }
+  if (L > 0) {
+    if (a->cu_seqlens) {
+      if (per_seq > L || a->segment_chunks > 0) {  // automatic: sequences average > 1 segment
+        pl.seg_len = L;
+        pl.seg_stride = (pl.max_chunks + L - 1) / L + a->N;
+      }
+    } else {
+      const int64_t P = per_seq > 0 ? (per_seq + L - 1) / L : 1;
+      if (P >= 2 || a->segment_chunks > 0) {
+        pl.seg_len = L;
+        pl.segs_per_seq = P;
+        pl.seg_stride = a->N * P;
+      }
+    }
+  }
+  pl.header = a->cu_seqlens ? round_up(static_cast<size_t>(a->N + 1) * 16, 256) : 0;
+  pl.records = pl.header;
+  size_t end = pl.records + static_cast<size_t>(pl.max_chunks) * static_cast<size_t>(a->H) *
+                                static_cast<size_t>(kda::kRecord);
+  if (pl.seg_len > 0) {
+    const size_t slots = static_cast<size_t>(a->H) * static_cast<size_t>(pl.seg_stride);
+    pl.scan_s = round_up(end, 256);
+    pl.scan_phi = pl.scan_s + slots * kda::kD * kda::kD * 4;
+    end = pl.scan_phi + slots * kda::kD * kda::kD * 2;
+  }
+  pl.total = end;
+  return pl;
+}
+
+size_t workspace_need(const kda_prefill_args* a) { return make_plan(a).total; }
+
+// Rows per workgroup of the recurrence launches: the explicit choice, else 64 in the
+// segmented form (launch A alone has about one workgroup per compute unit) and the
+// fill rule in the serial form.
+int rows_of(const kda_prefill_args* a, const Plan& pl, int num_cus) {
+  if (a->rows_per_workgroup) return a->rows_per_workgroup;
+  return pl.seg_len > 0 ? 64 : rows_per_wg(a, num_cus);
 }
 
 std::atomic<int> g_cu_count[64];
@@ -215,13 +284,25 @@ kda_status kda_prefill_plan(const kda_prefill_args* a, int32_t num_cus, kda_plan
   const kda_status s = check_shape(a);
   if (s != KDA_OK) return s;
   if (!out) return fail(KDA_ERR_NULL, "out is NULL");
-  const int rows = rows_per_wg(a, num_cus > 0 ? num_cus : 256);
+  const Plan pl = make_plan(a);
+  const int rows = rows_of(a, pl, num_cus > 0 ? num_cus : 256);
+  std::memset(out, 0, sizeof *out);
   out->rows_per_workgroup = rows;
-  out->waves_per_workgroup = rows / 16;
-  out->recurrence_workgroups = a->N * a->H * (KDA_HEAD_DIM / rows);
-  out->max_chunks = max_chunks_of(a);
-  out->prepare_workgroups = out->max_chunks * a->H;
-  out->workspace_header_bytes = header_bytes(a);
+  out->waves_per_workgroup = rows / 16 + kda::recurrence_loader_waves(rows / 16);
+  out->max_chunks = pl.max_chunks;
+  out->prepare_workgroups = pl.max_chunks * a->H;
+  out->workspace_header_bytes = pl.header;
+  out->segment_chunks = pl.seg_len;
+  out->segments_per_head_bound = pl.seg_stride;
+  if (pl.seg_len > 0) {
+    out->recurrence_workgroups = a->H * pl.seg_stride * (2 * KDA_HEAD_DIM / rows);
+    out->scan_c_workgroups = a->H * pl.seg_stride * (KDA_HEAD_DIM / rows);
+    out->combine_workgroups = a->H * a->N * 2;
+  } else {
+    out->recurrence_workgroups = a->N * a->H * (KDA_HEAD_DIM / rows);
+  }
+  out->scan_state_offset = pl.scan_s;
+  out->scan_transition_offset = pl.scan_phi;
   return KDA_OK;
 }
 
@@ -229,7 +310,9 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   kda_status s = kda_prefill_check(a);
   if (s != KDA_OK) return s;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const int rows = rows_per_wg(a, cu_count_current());
+  const Plan pl = make_plan(a);
+  const int rows = rows_of(a, pl, cu_count_current());
+  unsigned char* ws = static_cast<unsigned char*>(a->workspace);
 
   kda::Params p{};
   p.q = a->q;
@@ -243,31 +326,58 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   p.dt_bias = a->dt_bias;
   p.o = a->o;
   p.state_out = a->state_out;
-  p.cu_chunks = a->cu_seqlens ? static_cast<int64_t*>(a->workspace) : nullptr;
-  p.records = static_cast<unsigned char*>(a->workspace) + header_bytes(a);
+  p.cu_chunks = a->cu_seqlens ? reinterpret_cast<int64_t*>(ws) : nullptr;
+  p.cu_segs = a->cu_seqlens ? reinterpret_cast<int64_t*>(ws) + (a->N + 1) : nullptr;
+  p.records = ws + pl.records;
   p.B = a->B;
   p.T = a->T;
   p.H = a->H;
   p.N = a->N;
-  p.max_chunks = max_chunks_of(a);
+  p.max_chunks = pl.max_chunks;
   p.chunks_per_seq = (a->T + kda::kC - 1) / kda::kC;
   p.scale = a->scale > 0.0f ? a->scale : 1.0f / std::sqrt(static_cast<float>(KDA_HEAD_DIM));
   p.lower_bound = a->lower_bound;
   p.flags = a->flags;
   p.waves = rows / 16;
+  p.mode = kda::kModeSerial;
+  p.seg_len = pl.seg_len;
+  p.segs_per_seq = pl.segs_per_seq;
+  p.seg_stride = pl.seg_stride;
+  if (pl.seg_len > 0) {
+    p.scan_s = reinterpret_cast<float*>(ws + pl.scan_s);
+    p.scan_phi = reinterpret_cast<unsigned short*>(ws + pl.scan_phi);
+  }
   const bool io_bf16 = a->io_dtype == KDA_BF16;
   const bool st_bf16 = a->state_dtype == KDA_BF16;
-  const int64_t rec_wgs = a->N * a->H * (KDA_HEAD_DIM / rows);
   hipEvent_t* ev = nullptr;
   if (a->trace_events && a->n_trace_events >= 3)
     ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(a->trace_events));
+  const bool ev5 = ev && a->n_trace_events >= 5;
 
   hipError_t e = hipSuccess;
   if (ev) e = hipEventRecord(ev[0], stream);
   if (e == hipSuccess && a->cu_seqlens) e = kda::launch_plan(p, stream);
   if (e == hipSuccess && a->T > 0) e = kda::launch_prepare(p, io_bf16, stream);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
-  if (e == hipSuccess) e = kda::launch_recurrence(p, rec_wgs, io_bf16, st_bf16, stream);
+  if (pl.seg_len == 0) {
+    const int64_t wgs = a->N * a->H * (KDA_HEAD_DIM / rows);
+    if (e == hipSuccess) e = kda::launch_recurrence(p, wgs, io_bf16, st_bf16, stream);
+    if (e == hipSuccess && ev5) e = hipEventRecord(ev[3], stream);
+    if (e == hipSuccess && ev5) e = hipEventRecord(ev[4], stream);
+  } else {
+    p.mode = kda::kModeScanA;
+    p.blocks = 2 * KDA_HEAD_DIM / rows;
+    if (e == hipSuccess)
+      e = kda::launch_recurrence(p, a->H * pl.seg_stride * p.blocks, io_bf16, st_bf16, stream);
+    if (e == hipSuccess && ev5) e = hipEventRecord(ev[3], stream);
+    if (e == hipSuccess && (a->cu_seqlens || pl.segs_per_seq >= 3))
+      e = kda::launch_combine(p, stream);
+    if (e == hipSuccess && ev5) e = hipEventRecord(ev[4], stream);
+    p.mode = kda::kModeScanC;
+    p.blocks = KDA_HEAD_DIM / rows;
+    if (e == hipSuccess)
+      e = kda::launch_recurrence(p, a->H * pl.seg_stride * p.blocks, io_bf16, st_bf16, stream);
+  }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s", hipGetErrorString(e));
   return KDA_OK;

@@ -16,6 +16,12 @@ constexpr int kOffD = 12288;     // fp32 [128]
 constexpr int kOffMb = 12800;    // bf16 [64][4]
 constexpr int kOffAqk = 13312;   // bf16 [64][4]
 
+// Recurrence launch modes: one serial run per sequence, or the launches of the
+// segmented (time-parallel) form.
+constexpr int32_t kModeSerial = 0;
+constexpr int32_t kModeScanA = 1;  // segment 0 (true start) + Z_p, Phi_p of middle segments
+constexpr int32_t kModeScanC = 2;  // segments 1..P-1 again from their true start states
+
 constexpr uint32_t kFlagL2 = 1u << 0;
 constexpr uint32_t kFlagGate = 1u << 1;
 constexpr uint32_t kFlagBetaLogit = 1u << 2;
@@ -40,7 +46,16 @@ struct Params {
   float scale;
   float lower_bound;
   uint32_t flags;
-  int32_t waves;              // recurrence waves per workgroup (16 value rows each)
+  int32_t waves;              // recurrence compute waves per workgroup (16 rows each)
+  // Segmented form (modes A and C and the combine kernel).
+  int32_t mode;               // kModeSerial / kModeScanA / kModeScanC
+  int32_t blocks;             // row blocks per task of this launch (A: 256 / rows, C: 128 / rows)
+  int64_t seg_len;            // chunks per segment
+  int64_t segs_per_seq;       // fixed layout: segments per sequence
+  int64_t seg_stride;         // scan slots per head (bound on the total segment count)
+  int64_t* cu_segs;           // varlen: [N + 1] prefix of segments per sequence
+  float* scan_s;              // FP32 [H][seg_stride][128][128]: S_p, Z_p
+  unsigned short* scan_phi;   // BF16 [H][seg_stride][128 keys][128 rows]: Phi_p transposed
 };
 
 hipError_t launch_plan(const Params& p, hipStream_t stream);
@@ -48,5 +63,6 @@ hipError_t launch_prepare(const Params& p, bool io_bf16, hipStream_t stream);
 int recurrence_loader_waves(int compute_waves);
 hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16,
                              bool state_bf16, hipStream_t stream);
+hipError_t launch_combine(const Params& p, hipStream_t stream);
 
 }  // namespace kda

@@ -20,36 +20,51 @@
 
 namespace kda {
 
-// Exclusive prefix of ceil(len_n / 16) over the packed sequences: cu_chunks[0..N].
+// Exclusive prefixes over the packed sequences: cu_chunks[0..N] of ceil(len_n / 16),
+// and, when seg_len > 0, cu_segs[0..N] of max(1, ceil(chunks_n / seg_len)) (the number
+// of time segments of sequence n; a zero-length sequence keeps one empty segment so its
+// state passes through).
 __global__ __launch_bounds__(256) void kda_plan_kernel(const int64_t* __restrict__ cu,
-                                                        int64_t N,
-                                                        int64_t* __restrict__ cu_chunks) {
-  __shared__ int64_t buf[256];
-  __shared__ int64_t carry;
+                                                        int64_t N, int64_t seg_len,
+                                                        int64_t* __restrict__ cu_chunks,
+                                                        int64_t* __restrict__ cu_segs) {
+  __shared__ int64_t buf[2][256];
+  __shared__ int64_t carry[2];
   const int t = threadIdx.x;
   if (t == 0) {
-    carry = 0;
+    carry[0] = carry[1] = 0;
     cu_chunks[0] = 0;
+    if (seg_len > 0) cu_segs[0] = 0;
   }
   __syncthreads();
   for (int64_t base = 0; base < N; base += 256) {
     const int64_t i = base + t;
-    int64_t c = 0;
+    int64_t c = 0, sg = 0;
     if (i < N) {
       const int64_t len = cu[i + 1] - cu[i];
       c = len > 0 ? (len + kC - 1) / kC : 0;
+      if (seg_len > 0) sg = c > 0 ? (c + seg_len - 1) / seg_len : 1;
     }
-    buf[t] = c;
+    buf[0][t] = c;
+    buf[1][t] = sg;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
-      const int64_t x = t >= off ? buf[t - off] : 0;
+      const int64_t x0 = t >= off ? buf[0][t - off] : 0;
+      const int64_t x1 = t >= off ? buf[1][t - off] : 0;
       __syncthreads();
-      buf[t] += x;
+      buf[0][t] += x0;
+      buf[1][t] += x1;
       __syncthreads();
     }
-    if (i < N) cu_chunks[i + 1] = carry + buf[t];
+    if (i < N) {
+      cu_chunks[i + 1] = carry[0] + buf[0][t];
+      if (seg_len > 0) cu_segs[i + 1] = carry[1] + buf[1][t];
+    }
     __syncthreads();
-    if (t == 0) carry += buf[255];
+    if (t == 0) {
+      carry[0] += buf[0][255];
+      carry[1] += buf[1][255];
+    }
     __syncthreads();
   }
 }
@@ -315,8 +330,9 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
 }
 
 hipError_t launch_plan(const Params& p, hipStream_t stream) {
+  const int64_t seg_len = p.seg_len;  // 0: serial recurrence, no segment prefix
   hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.N,
-                     p.cu_chunks);
+                     seg_len, p.cu_chunks, p.cu_segs);
   return hipGetLastError();
 }
 

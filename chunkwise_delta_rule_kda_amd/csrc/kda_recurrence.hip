@@ -1,4 +1,4 @@
-// kda_recurrence: the serial state carry across chunks.
+// kda_recurrence: the state carry across chunks, serial or in time-parallel segments.
 //
 // The "FlashKDA column split" post, section 3.1 ("Every value column is independent"),
 // shows that in the transposed form
@@ -19,23 +19,33 @@
 //   O     = S_old Qt^T + UV^T A_qk^T    (uses the entering state only)
 // State is FP32 in registers; MFMA operands are BF16.
 //
-// Workgroup. W compute waves (16 value rows each, W = 1, 2, 4, 8) of one
-// (sequence, head) plus L loader waves (L = 4 - W when W < 4). Every chunk's record and
-// V tile are fetched once per workgroup by all of its waves together with ordinary
-// 16-byte loads (one wave alone streams only ~40 GB/s, four reach the compute unit's
-// ~150 GB/s; the LDS-DMA path was measured at ~16 B/clock), two chunks ahead, and
-// staged through a 3-slot LDS ring. One raw s_barrier per chunk (after each wave's own
-// LDS writes have completed; no memory fence, so the global loads in flight stay in
-// flight) publishes the next slot.
+// Segments. The carry is affine in the state: over a run of chunks, S_end = S_start Phi
+// + Z, where Z is the end state of the run started from zero and Phi (128 x 128, keys x
+// keys) the end state of the run started from the identity with V = 0 (rows of S never
+// interact, so Phi's rows are computed exactly like value rows). A sequence cut into
+// segments 0..P-1 of L chunks is evaluated in three launches:
+//   A: segment 0 from the true initial state (writing its O and S_1), and, for
+//      segments 1..P-2, Z_p and Phi_p;
+//   B: S_{p+1} = S_p Phi_p + Z_p for p = 1..P-2 (kda_combine_kernel);
+//   C: segments 1..P-1 again from S_p, writing O and, for the last one, the final state.
+// Workgroups of launch A see a 256-row space: rows 0..127 are value rows (Z or the true
+// run), rows 128..255 the rows of Phi. Serial mode (one segment per sequence) is the
+// single launch of the plain recurrence.
 //
-// Ring protocol, iteration c (all waves):
-//   write the registers holding chunk c+1 into slot (c+1)%3     [slot of chunk c-2]
-//   issue the loads of chunk c+2 into registers
-//   wait for own LDS writes; barrier B_c                         [chunk c+1 visible]
-//   compute waves: read chunk c+1's chain inputs (prefetch) and compute chunk c.
-// Chunk c-2's slot is rewritten only after B_{c-1}, which every wave reaches after its
-// last read of chunk c-2 (made in iteration c-2). Chunk c's operands used after B_c were
-// written before B_{c-1}.
+// Workgroup. W compute waves (16 value rows each, W = 1, 2, 4) plus NL loader waves.
+// The loaders stream each chunk's record and V tile with 16-byte loads, DEPTH chunks
+// ahead in registers, into a 3-slot LDS ring; one s_barrier per chunk publishes a slot.
+// (One workgroup streams at most ~60 GB/s; two loader waves with three or more chunks
+// in flight reach that, one wave or one chunk in flight does not, and LDS-DMA loads
+// deliver only ~16 B/clock.) Compute waves touch LDS and registers only.
+//
+// Ring protocol, iteration c:
+//   loaders: write chunk c+1 into slot (c+1)%3, issue the loads of chunk c+1+DEPTH,
+//            wait for their own LDS writes, barrier B_c;
+//   compute: read chunk c's tail operands (slot c%3), store the O of chunk c-1, wait
+//            for own LDS reads, barrier B_c, read chunk c+1's chain operands, compute c.
+// Slot (c+1)%3 last held chunk c-2, whose final reads happened before B_{c-2}; the
+// loaders write it after B_{c-1}.
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -46,21 +56,6 @@ namespace {
 
 constexpr int kSlots = 3;
 constexpr int kRecUnits = kRecord / 16;  // 864 sixteen-byte units per record
-
-// Padded ring-slot bytes for W compute waves (loader waves fill the workgroup to at
-// least 4 waves), element size es: ceil((864 + 16 W es) / threads) * threads * 16.
-constexpr int slot_bytes(int w, int es) {
-  const int nt = 64 * (w < 4 ? 4 : w);
-  const int real = kRecUnits + 16 * w * es;
-  return (real + nt - 1) / nt * nt * 16;
-}
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int kMaxSlotBytes =
-    cmax(cmax(cmax(slot_bytes(1, 4), slot_bytes(2, 4)), cmax(slot_bytes(4, 4), slot_bytes(8, 4))),
-         cmax(cmax(slot_bytes(1, 2), slot_bytes(2, 2)), cmax(slot_bytes(4, 2), slot_bytes(8, 2))));
-static_assert(kMaxSlotBytes == 24576, "slot size table");
-static_assert(slot_bytes(4, 4) / 16 / 256 <= 5 && slot_bytes(8, 4) / 16 / 512 <= 5,
-              "kMaxLoads covers every configuration");
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -75,52 +70,178 @@ __device__ __forceinline__ void lds_barrier() {
   compiler_fence();
 }
 
+constexpr int loader_waves(int w) { return w < 4 ? 2 : 4; }
+constexpr int block_threads(int w) { return 64 * (w + loader_waves(w)); }
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 template <bool BF16IO, int W>
 struct Tile {
+  static constexpr int NL = loader_waves(W);              // loader waves
   static constexpr int ES = BF16IO ? 2 : 4;
-  static constexpr int NT = 64 * (W < 4 ? 4 : W);        // threads in the workgroup
+  static constexpr int NT = 64 * (W + NL);                // threads in the workgroup
+  static constexpr int LT = 64 * NL;                      // loader threads
   static constexpr int VROW = 16 * W * ES;                // bytes of one V-tile token row
   static constexpr int PARTS = VROW / 16;                 // 16-byte pieces per token row
   static constexpr int REAL = kRecUnits + VROW;           // record + V-tile units (16 B)
-  static constexpr int K = (REAL + NT - 1) / NT;          // loads per thread per chunk
-  static constexpr int SLOT = K * NT * 16;                // padded slot: K units per thread
-  static_assert(SLOT == slot_bytes(W, ES) && SLOT <= kMaxSlotBytes, "slot table");
+  static constexpr int K = (REAL + LT - 1) / LT;          // loads per loader thread per chunk
+  static constexpr int DEPTH = K <= 5 ? 4 : 3;            // chunks in flight per loader
+  static constexpr int SLOT = K * LT * 16;                // padded ring slot
+  static_assert(K * (DEPTH - 1) <= 63, "vmcnt range");
+  static_assert(DEPTH == 3 || DEPTH == 4, "loader unrolling");
+  static_assert(kSlots * SLOT <= 65536, "LDS ring");
 };
 
-// One thread's share of a chunk's global -> LDS copy. Unit u = tid + k * NT of a chunk
-// is record byte 16 u (u < 864), V-tile piece u - 864 (token row, 16-byte part), or
-// padding (re-reads record unit 0 into the slot's unused tail).
-template <bool BF16IO, int W>
-struct Loader {
-  using T = Tile<BF16IO, W>;
-  u32x4 r[T::K];
+// Where one workgroup's run starts, what it reads and what it writes.
+enum StartKind : int { kStartIn = 0, kStartZero = 1, kStartIdentity = 2, kStartScan = 3 };
 
-  __device__ __forceinline__ void issue(int tid, const unsigned char* rec,
-                                        const unsigned char* vrow0, int64_t vstride_b,
-                                        int64_t nvalid) {
-#pragma unroll
-    for (int k = 0; k < T::K; ++k) {
-      const int u = tid + k * T::NT;
-      const int i = u - kRecUnits;
-      const unsigned char* src;
-      if (i >= 0 && i < T::VROW) {
-        const int tok = i / T::PARTS;
-        const int part = i - tok * T::PARTS;
-        src = vrow0 + (tok < nvalid ? tok : 0) * vstride_b + part * 16;  // pad rows: row 0
-      } else {
-        src = rec + (u < kRecUnits ? u * 16 : 0);
-      }
-      r[k] = *reinterpret_cast<const u32x4*>(src);
+struct Task {
+  int64_t tok0;       // first token of the run (row index into [B*T] / packed tokens)
+  int64_t tok_end;    // end token of the run's sequence
+  int64_t rec_chunk;  // index of the run's first record in the head's record stream
+  int64_t nch;        // chunks in the run
+  int64_t sh;         // sequence * H + head
+  int64_t h;
+  int vwg;            // first row of the workgroup within its 128-row space
+  int start;          // StartKind
+  bool vzero;         // V = 0 (rows of Phi)
+  bool out;           // write O
+  bool final_state;   // write state_out
+  const float* s_src; // kStartScan: FP32 [128][128] start state
+  float* s_dst;       // FP32 [128][128] end state (scan), or null
+  unsigned short* phi_dst;  // BF16 [128 keys][128 rows] end state transposed, or null
+};
+
+__device__ __forceinline__ int64_t task_index() {
+  // XCD-aware order: workgroup b runs on XCD b % 8; consecutive tasks (the row blocks of
+  // one run, which read the same records) go to the same XCD's L2.
+  const int64_t total = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  return (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
+}
+
+// Token and chunk range of sequence n (the varlen plan's prefix, or the fixed layout).
+__device__ __forceinline__ void seq_range(const Params& p, int64_t n, int64_t& start,
+                                          int64_t& end, int64_t& chunk0, int64_t& nch) {
+  if (p.cu_seqlens) {
+    start = p.cu_seqlens[n];
+    end = min(p.cu_seqlens[n + 1], p.T);
+    chunk0 = p.cu_chunks[n];
+  } else {
+    start = n * p.T;
+    end = start + p.T;
+    chunk0 = n * p.chunks_per_seq;
+  }
+  nch = end > start ? (end - start + kC - 1) / kC : 0;
+  if (chunk0 < 0) nch = 0;
+  if (chunk0 + nch > p.max_chunks) nch = p.max_chunks > chunk0 ? p.max_chunks - chunk0 : 0;
+}
+
+// Segments of sequence n and the global index of its first one.
+__device__ __forceinline__ void seq_segments(const Params& p, int64_t n, int64_t& first,
+                                             int64_t& count) {
+  if (p.cu_seqlens) {
+    first = p.cu_segs[n];
+    count = p.cu_segs[n + 1] - first;
+  } else {
+    first = n * p.segs_per_seq;
+    count = p.segs_per_seq;
+  }
+}
+
+__device__ bool decode_task(const Params& p, int rows, Task& t) {
+  const int64_t task = task_index();
+  const int64_t H = p.H;
+  t.vzero = false;
+  t.out = true;
+  t.final_state = true;
+  t.s_src = nullptr;
+  t.s_dst = nullptr;
+  t.phi_dst = nullptr;
+  if (p.mode == kModeSerial) {
+    const int blocks = kD / rows;
+    const int64_t sh = task / blocks;
+    const int blk = static_cast<int>(task - sh * blocks);
+    const int64_t n = sh / H;
+    if (n >= p.N) return false;
+    int64_t start, end, chunk0, nch;
+    seq_range(p, n, start, end, chunk0, nch);
+    t.tok0 = start;
+    t.tok_end = end;
+    t.rec_chunk = chunk0;
+    t.nch = nch;
+    t.sh = sh;
+    t.h = sh - n * H;
+    t.vwg = blk * rows;
+    t.start = kStartIn;
+    return true;
+  }
+  const int blocks = p.blocks;
+  const int64_t per_head = p.seg_stride * blocks;
+  const int64_t h = task / per_head;
+  const int64_t rem = task - h * per_head;
+  const int64_t gsg = rem / blocks;
+  const int blk = static_cast<int>(rem - gsg * blocks);
+  if (h >= H) return false;
+  int64_t n;
+  if (p.cu_seqlens) {
+    if (gsg >= p.cu_segs[p.N]) return false;
+    int64_t lo = 0, hi = p.N - 1;  // largest n with cu_segs[n] <= gsg
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (p.cu_segs[mid] <= gsg) lo = mid;
+      else hi = mid - 1;
     }
+    n = lo;
+  } else {
+    n = gsg / p.segs_per_seq;
+    if (n >= p.N) return false;
   }
-
-  __device__ __forceinline__ void store(int tid, lds_u8* slot) const {
-#pragma unroll
-    for (int k = 0; k < T::K; ++k)
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(slot + (tid + k * T::NT) * 16) =
-          r[k];
+  int64_t first, nseg, start, end, chunk0, nch;
+  seq_segments(p, n, first, nseg);
+  seq_range(p, n, start, end, chunk0, nch);
+  const int64_t seg = gsg - first;
+  if (seg < 0 || seg >= nseg || first + nseg > p.seg_stride) return false;
+  const int64_t c0 = seg * p.seg_len;
+  const int64_t c1 = min(c0 + p.seg_len, nch);
+  t.tok0 = start + c0 * kC;
+  t.tok_end = end;
+  t.rec_chunk = chunk0 + c0;
+  t.nch = c1 > c0 ? c1 - c0 : 0;
+  t.sh = n * H + h;
+  t.h = h;
+  const int64_t slot = h * p.seg_stride + gsg;  // scan slot of this segment
+  const int vr = blk * rows;
+  if (p.mode == kModeScanA) {
+    if (nseg >= 2 && seg == nseg - 1) return false;  // last segment: only in launch C
+    if (vr < kD) {
+      t.vwg = vr;
+      t.start = seg == 0 ? kStartIn : kStartZero;
+      t.out = seg == 0;
+      t.final_state = nseg == 1;
+      if (nseg >= 2) t.s_dst = p.scan_s + (slot + 1) * (kD * kD);  // S_1, or Z_seg
+    } else {
+      if (seg == 0) return false;
+      t.vwg = vr - kD;
+      t.start = kStartIdentity;
+      t.vzero = true;
+      t.out = false;
+      t.final_state = false;
+      t.phi_dst = p.scan_phi + slot * (kD * kD);
+    }
+    return true;
   }
-};
+  // launch C
+  if (seg == 0) return false;
+  t.vwg = vr;
+  t.start = kStartScan;
+  t.s_src = p.scan_s + slot * (kD * kD);
+  t.final_state = seg == nseg - 1;
+  return true;
+}
 
 struct ChainIn {  // needed at the very start of a chunk (read one chunk ahead)
   bf16x8 kn[4];
@@ -150,13 +271,13 @@ __device__ __forceinline__ void read_chain(ChainIn& x, const lds_u8* slot, int l
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tok = 4 * grp + j;
-    const lds_u8* p = slot + kRecord + tok * T::VROW + (16 * w + m) * T::ES;
+    const lds_u8* q = slot + kRecord + tok * T::VROW + (16 * w + m) * T::ES;
     short s;
     if constexpr (BF16IO)
-      s = *reinterpret_cast<const __attribute__((address_space(3))) short*>(p);
+      s = *reinterpret_cast<const __attribute__((address_space(3))) short*>(q);
     else
       s = static_cast<short>(float_to_bf16_bits(
-          *reinterpret_cast<const __attribute__((address_space(3))) float*>(p)));
+          *reinterpret_cast<const __attribute__((address_space(3))) float*>(q)));
     x.vv[j] = tok < nvalid ? s : static_cast<short>(0);
   }
 }
@@ -205,124 +326,282 @@ __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f
   return out;
 }
 
-template <bool BF16IO, bool BF16ST, int W>
-__global__ __launch_bounds__(64 * (W < 4 ? 4 : W)) void kda_recurrence_kernel(Params p) {
+// Loader waves: the run's chunks, global -> registers (DEPTH chunks ahead) -> LDS ring.
+// Unit u = lt + k * LT of a chunk is record byte 16 u (u < 864), V-tile piece u - 864
+// (token row, 16-byte part), or padding (re-reads record unit 0 into the slot's unused
+// tail). Chunks past the run's end re-read its last chunk (in bounds, never used).
+template <bool BF16IO, int W>
+__device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_u8* ring,
+                                            int lt) {
   using T = Tile<BF16IO, W>;
-  __shared__ __attribute__((aligned(16))) unsigned char ring_[kSlots * T::SLOT];
-  lds_u8* ring = (lds_u8*)(ring_);  // address-space cast
+  const int64_t vstride_b = p.H * kD * T::ES;
+  const unsigned char* rec0 =
+      p.records + (t.h * p.max_chunks + t.rec_chunk) * static_cast<int64_t>(kRecord);
+  const int vcol = t.vzero ? 0 : t.vwg;  // Phi rows read no V (any in-bounds address)
+  const unsigned char* v0 = static_cast<const unsigned char*>(p.v) +
+                            (t.tok0 * p.H * kD + t.h * kD + vcol) * T::ES;
+  const int64_t vchunk_b = kC * vstride_b;
+  const int64_t nch = t.nch;
+  // Per-unit source offsets that do not depend on the chunk.
+  int64_t off[T::K];
+  int vtok[T::K];  // V token row of the unit, or -1 for a record unit
+#pragma unroll
+  for (int k = 0; k < T::K; ++k) {
+    const int u = lt + k * T::LT;
+    const int i = u - kRecUnits;
+    if (i >= 0 && i < T::VROW && !t.vzero) {
+      const int tok = i / T::PARTS;
+      vtok[k] = tok;
+      off[k] = (i - tok * T::PARTS) * 16;
+    } else {
+      vtok[k] = -1;
+      off[k] = u < kRecUnits ? u * 16 : 0;
+    }
+  }
+  u32x4 r[T::DEPTH][T::K];
+  auto issue = [&](u32x4(&dst)[T::K], int64_t j) {
+    j = j < nch - 1 ? j : nch - 1;
+    const unsigned char* rec = rec0 + j * kRecord;
+    const unsigned char* vt = v0 + j * vchunk_b;
+    const int64_t nvalid = t.tok_end - (t.tok0 + j * kC);
+#pragma unroll
+    for (int k = 0; k < T::K; ++k) {
+      const unsigned char* src;
+      if (vtok[k] >= 0)
+        src = vt + (vtok[k] < nvalid ? vtok[k] : 0) * vstride_b + off[k];  // pad rows: row 0
+      else
+        src = rec + off[k];
+      dst[k] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  auto put = [&](const u32x4(&src)[T::K], int slot) {
+    lds_u8* s = ring + slot * T::SLOT;
+#pragma unroll
+    for (int k = 0; k < T::K; ++k)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(s + (lt + k * T::LT) * 16) =
+          src[k];
+  };
+#pragma unroll
+  for (int d = 0; d < T::DEPTH; ++d) issue(r[d], d);
+  put(r[0], 0);
+  issue(r[0], T::DEPTH);
+  lds_barrier();  // B_{-1}: chunk 0 visible
+  int slot = 0;  // slot of chunk c
+  // Iteration c: chunk c + 1 (register set (c + 1) % DEPTH) into the ring, chunk
+  // c + 1 + DEPTH into that set, barrier B_c. Whole groups of DEPTH iterations are
+  // unrolled without conditions so that the compiler's wait before each LDS write is
+  // for the oldest set only (DEPTH - 1 chunks stay in flight).
+  auto step = [&](auto set_c, int64_t c) {
+    constexpr int set = decltype(set_c)::value;
+    slot = slot + 1 == kSlots ? 0 : slot + 1;  // slot of chunk c + 1
+    put(r[set], slot);
+    issue(r[set], c + 1 + T::DEPTH);
+    lds_barrier();  // B_c
+  };
+  int64_t c0 = 0;
+#pragma unroll 1
+  for (; c0 + T::DEPTH <= nch; c0 += T::DEPTH) {
+    step(IntC<1 % T::DEPTH>{}, c0);
+    step(IntC<2 % T::DEPTH>{}, c0 + 1);
+    step(IntC<3 % T::DEPTH>{}, c0 + 2);
+    if constexpr (T::DEPTH == 4) step(IntC<0>{}, c0 + 3);
+  }
+  const int64_t rest = nch - c0;  // 0 .. DEPTH - 1
+  if (rest > 0) step(IntC<1 % T::DEPTH>{}, c0);
+  if (rest > 1) step(IntC<2 % T::DEPTH>{}, c0 + 1);
+  if constexpr (T::DEPTH == 4)
+    if (rest > 2) step(IntC<3>{}, c0 + 2);
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  // W compute waves; the rest of the workgroup loads only.
-  const int slices = 8 / W;
-  // XCD-aware order: workgroup b runs on XCD b % 8, so consecutive tasks (the slices of
-  // one head, which read the same records) are mapped to the same XCD's L2.
-  const int64_t total = gridDim.x;
-  const int64_t bid = blockIdx.x;
-  const int64_t task = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
-  const int64_t sh = task / slices;
-  const int slice = static_cast<int>(task - sh * slices);
-  const int64_t H = p.H;
-  const int64_t s = sh / H;
-  const int64_t h = sh - s * H;
-  const int vwg = slice * 16 * W;  // first value row of this workgroup
-  const bool compute = wave < W;
-  const int v0 = vwg + 16 * wave;
+template <bool BF16IO, bool BF16ST, int W>
+__device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds_u8* ring,
+                                             int wave, int lane) {
+  using T = Tile<BF16IO, W>;
   const int m = lane & 15;
   const int grp = lane >> 4;
-
-  int64_t start, end, chunk0;
-  if (p.cu_seqlens) {
-    start = p.cu_seqlens[s];
-    end = min(p.cu_seqlens[s + 1], p.T);
-    chunk0 = p.cu_chunks[s];
-  } else {
-    start = s * p.T;
-    end = start + p.T;
-    chunk0 = s * p.chunks_per_seq;
-  }
-  int64_t nch = end > start ? (end - start + kC - 1) / kC : 0;
-  if (chunk0 < 0) nch = 0;
-  if (chunk0 + nch > p.max_chunks) nch = p.max_chunks > chunk0 ? p.max_chunks - chunk0 : 0;
-
-  const int64_t vstride = H * kD;
-  const int64_t vstride_b = vstride * T::ES;
-  const unsigned char* rec0 =
-      p.records + (h * p.max_chunks + chunk0) * static_cast<int64_t>(kRecord);
-  const unsigned char* vtile0 = static_cast<const unsigned char*>(p.v) +
-                                (start * vstride + h * kD + vwg) * T::ES;
-  const int64_t vchunk_b = kC * vstride_b;  // bytes between consecutive chunks of V
-  Loader<BF16IO, W> ld;
-  // Next chunk to fetch (clamped: past the end re-reads the last chunk, in bounds).
-  int64_t fetch = 0;
-  auto issue_next = [&]() {
-    const int64_t j = fetch < nch - 1 ? fetch : nch - 1;
-    ld.issue(tid, rec0 + j * kRecord, vtile0 + j * vchunk_b, vstride_b, end - start - j * kC);
-    ++fetch;
-  };
+  const int v0 = t.vwg + 16 * wave;  // first row of this wave
+  const int64_t nch = t.nch;
 
   // State rows v0 + m, keys 16 b + 4 grp + j: the 16x16x16 accumulator layout.
-  const int64_t srow = ((s * H + h) * kD + v0 + m) * kD;
+  const int64_t srow = (t.sh * kD + v0 + m) * kD;
+  const int64_t lrow = (v0 + m) * kD;  // row in a scan slot
   f32x4 st[8];
   bf16x8 sp[4];
-  if (compute) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      if (p.state_in)
-        st[b] = load4<BF16ST>(p.state_in, srow + 16 * b + 4 * grp);
-      else
-        st[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < 8; ++b) {
+    const int key = 16 * b + 4 * grp;
+    if (t.start == kStartIn && p.state_in) {
+      st[b] = load4<BF16ST>(p.state_in, srow + key);
+    } else if (t.start == kStartScan) {
+      st[b] = load4<false>(t.s_src, lrow + key);
+    } else if (t.start == kStartIdentity) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st[b][j] = (v0 + m == key + j) ? 1.f : 0.f;
+    } else {
+      st[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sp[kb] = pack8(st[2 * kb], st[2 * kb + 1]);
   }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) sp[kb] = pack8(st[2 * kb], st[2 * kb + 1]);
 
+  const int64_t vstride = p.H * kD;
+  auto nvalid_of = [&](int64_t c) -> int64_t {
+    return t.vzero ? 0 : t.tok_end - (t.tok0 + c * kC);
+  };
   if (nch > 0) {
-    issue_next();            // chunk 0
-    ld.store(tid, ring);     // slot 0
-    issue_next();            // chunk 1
-    lds_barrier();           // chunk 0 visible
+    lds_barrier();  // B_{-1}: chunk 0 visible
     ChainIn cur;
-    if (compute) read_chain<BF16IO, W>(cur, ring, lane, wave, end - start);
+    read_chain<BF16IO, W>(cur, ring, lane, wave, nvalid_of(0));
     int cs = 0;  // slot of chunk c
-    // O of chunk c is stored at the start of iteration c + 1, before the next loads are
-    // issued: loads and stores retire through one in-order counter, so a wait for a
-    // load never waits for a store issued after it.
+    // O of chunk c is stored at the start of iteration c + 1, before the barrier: loads
+    // and stores retire through one in-order counter, so a later wait for this wave's
+    // loads never waits for this store.
     f32x4 pend = {0.f, 0.f, 0.f, 0.f};
-    const int64_t obase = start * vstride + h * kD + v0;
+    const int64_t obase = t.tok0 * vstride + t.h * kD + v0;
     auto store_out = [&](int64_t c) {
-      if (m < end - start - c * kC)
+      if (m < t.tok_end - (t.tok0 + c * kC))
         store4<BF16IO>(p.o, obase + (c * kC + m) * vstride + 4 * grp, pend);
     };
 #pragma unroll 1
     for (int64_t c = 0; c < nch; ++c) {
-      const int ns = cs + 1 == kSlots ? 0 : cs + 1;     // slot of chunk c + 1
-      const lds_u8* slot = ring + cs * T::SLOT;
+      const int ns = cs + 1 == kSlots ? 0 : cs + 1;  // slot of chunk c + 1
       TailIn tail;
-      if (compute) read_tail(tail, slot, lane);        // written before B_{c-1}
-      ld.store(tid, ring + ns * T::SLOT);              // chunk c + 1 (slot of chunk c - 2)
-      if (compute && c > 0) store_out(c - 1);
-      issue_next();                                    // chunk c + 2
-      lds_barrier();                                   // B_c: chunk c + 1 visible
-      if (compute) {
-        ChainIn nxt;
-        read_chain<BF16IO, W>(nxt, ring + ns * T::SLOT, lane, wave,
-                              end - start - (c + 1) * kC);
-        pend = chunk_step(cur, tail, st, sp);
-        cur = nxt;
-      }
+      read_tail(tail, ring + cs * T::SLOT, lane);
+      if (t.out && c > 0) store_out(c - 1);
+      lds_barrier();  // B_c: chunk c + 1 visible
+      ChainIn nxt;
+      read_chain<BF16IO, W>(nxt, ring + ns * T::SLOT, lane, wave, nvalid_of(c + 1));
+      pend = chunk_step(cur, tail, st, sp);
+      cur = nxt;
       cs = ns;
     }
-    if (compute) store_out(nch - 1);
+    if (t.out) store_out(nch - 1);
   }
 
-  if (compute && p.state_out) {
+  if (t.final_state && p.state_out) {
 #pragma unroll
     for (int b = 0; b < 8; ++b) store4<BF16ST>(p.state_out, srow + 16 * b + 4 * grp, st[b]);
   }
+  if (t.s_dst) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) store4<false>(t.s_dst, lrow + 16 * b + 4 * grp, st[b]);
+  }
+  if (t.phi_dst) {  // transposed: [key][row]
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        t.phi_dst[(16 * b + 4 * grp + j) * kD + v0 + m] = float_to_bf16_bits(st[b][j]);
+  }
 }
 
+template <bool BF16IO, bool BF16ST, int W>
+__global__ __launch_bounds__(block_threads(W)) void kda_recurrence_kernel(Params p) {
+  using T = Tile<BF16IO, W>;
+  static_assert(T::NT == block_threads(W), "block size");
+  __shared__ __attribute__((aligned(16))) unsigned char ring_[kSlots * T::SLOT];
+  lds_u8* ring = (lds_u8*)(ring_);  // address-space cast
+
+  Task t;
+  if (!decode_task(p, 16 * W, t)) return;  // uniform over the workgroup
+  // The wave index as a scalar, so that the role branch below is uniform per wave.
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  if (wave < W)
+    compute_loop<BF16IO, BF16ST, W>(p, t, ring, wave, lane);
+  else if (t.nch > 0)
+    loader_loop<BF16IO, W>(p, t, ring, static_cast<int>(threadIdx.x) - 64 * W);
+}
+
+// Launch B of the segmented form: S_{p+1} = S_p Phi_p + Z_p, p = 1 .. P-2, for 64 value
+// rows of one (sequence, head) per workgroup (4 waves x 16 rows). In the transposed
+// form S^T_{p+1} = Phi_p^T S_p^T + Z_p^T the accumulator of one step is, after BF16
+// packing, the B operand of the next (the key permutation the recurrence uses), and
+// Phi_p^T (stored [key][row] by launch A) is the A operand, staged through LDS.
+constexpr int kPhiRow = kD * 2 + 16;  // LDS row pitch of Phi^T (bytes), padded for banks
+
+__global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) unsigned char phi_[kD * kPhiRow];
+  lds_u8* phi = (lds_u8*)(phi_);
+  const int64_t task = blockIdx.x;  // (h * N + n) * 2 + half
+  const int half = static_cast<int>(task & 1);
+  const int64_t hn = task >> 1;
+  const int64_t h = hn / p.N;
+  const int64_t n = hn - h * p.N;
+  if (h >= p.H) return;
+  int64_t first, nseg;
+  seq_segments(p, n, first, nseg);
+  if (nseg < 3 || first < 0 || first + nseg > p.seg_stride) return;  // nothing to combine
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int m = lane & 15;
+  const int grp = lane >> 4;
+  const int v0 = half * 64 + 16 * wave;
+  const int64_t lrow = (v0 + m) * kD;
+  const int64_t slot0 = h * p.seg_stride + first;
+  float* sbase = p.scan_s + slot0 * (kD * kD);
+  const unsigned short* pbase = p.scan_phi + slot0 * (kD * kD);
+
+  f32x4 st[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) st[b] = load4<false>(sbase + 1 * (kD * kD), lrow + 16 * b + 4 * grp);
+  // Phi^T rows (keys) of 256 B: thread tid copies 16-byte pieces tid + 256 i, i < 8.
+  u32x4 pr[8];
+  auto fetch_phi = [&](int64_t s) {
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(pbase + s * (kD * kD));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      pr[i] = *reinterpret_cast<const u32x4*>(src + (tid + 256 * i) * 16);
+  };
+  f32x4 z[8];
+  auto fetch_z = [&](int64_t s) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) z[b] = load4<false>(sbase + s * (kD * kD), lrow + 16 * b + 4 * grp);
+  };
+  fetch_phi(1);
+  fetch_z(2);
+#pragma unroll 1
+  for (int64_t s = 1; s + 1 < nseg; ++s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int piece = tid + 256 * i;  // 16 pieces per key row
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          phi + (piece >> 4) * kPhiRow + (piece & 15) * 16) = pr[i];
+    }
+    f32x4 zc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) zc[b] = z[b];
+    lds_barrier();
+    if (s + 2 < nseg) {  // prefetch the next step's operands
+      fetch_phi(s + 1);
+      fetch_z(s + 2);
+    }
+    bf16x8 sp[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sp[kb] = pack8(st[2 * kb], st[2 * kb + 1]);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      // A[key 16 b + m][r] with r = 32 kk + 16 (e / 4) + 4 grp + e % 4 (the B layout).
+      const lds_u8* row = phi + (16 * b + m) * kPhiRow + 8 * grp;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const i16x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) i16x4*>(
+            row + kk * 64);
+        const i16x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) i16x4*>(
+            row + kk * 64 + 32);
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc = mfma32(a, sp[kk], acc);
+      }
+      st[b] = acc + zc[b];
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) store4<false>(sbase + (s + 1) * (kD * kD), lrow + 16 * b + 4 * grp, st[b]);
+    lds_barrier();  // every wave is done with this Phi before the next is written
+  }
+}
 
 template <bool BF16IO, bool BF16ST>
 void launch_io(const Params& p, dim3 grid, hipStream_t stream) {
@@ -335,27 +614,22 @@ void launch_io(const Params& p, dim3 grid, hipStream_t stream) {
       hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 2>), grid,
                          dim3(Tile<BF16IO, 2>::NT), 0, stream, p);
       break;
-    case 4:
+    default:
       hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 4>), grid,
                          dim3(Tile<BF16IO, 4>::NT), 0, stream, p);
-      break;
-    default:
-      hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 8>), grid,
-                         dim3(Tile<BF16IO, 8>::NT), 0, stream, p);
       break;
   }
 }
 
 }  // namespace
 
-int recurrence_loader_waves(int compute_waves) {
-  return compute_waves < 4 ? 4 - compute_waves : 0;
-}
+int recurrence_loader_waves(int compute_waves) { return loader_waves(compute_waves); }
 
 hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16, bool state_bf16,
                              hipStream_t stream) {
   if (workgroups <= 0) return hipSuccess;
-  if (p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != 8) return hipErrorInvalidValue;
+  if (p.waves != 1 && p.waves != 2 && p.waves != 4) return hipErrorInvalidValue;
+  if (workgroups > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(workgroups));
   if (io_bf16) {
     if (state_bf16) launch_io<true, true>(p, grid, stream);
@@ -364,6 +638,15 @@ hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16, 
     if (state_bf16) launch_io<false, true>(p, grid, stream);
     else launch_io<false, false>(p, grid, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Params& p, hipStream_t stream) {
+  const int64_t wgs = p.H * p.N * 2;
+  if (wgs <= 0) return hipSuccess;
+  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kda_combine_kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream,
+                     p);
   return hipGetLastError();
 }
 

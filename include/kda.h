@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 #define KDA_HEAD_DIM 128 /* d_k = d_v = 128 */
 #define KDA_CHUNK 16     /* tokens per chunk */
 
@@ -63,7 +63,8 @@ typedef enum kda_status {
   KDA_ERR_WORKSPACE = 7,  /* workspace NULL, too small or not 256-byte aligned */
   KDA_ERR_HIP = 8,        /* a HIP runtime call or kernel launch failed */
   KDA_ERR_CU_SEQLENS = 9, /* kda_debug_check_cu_seqlens found a contract violation */
-  KDA_ERR_CONFIG = 10     /* rows_per_workgroup not one of 0, 16, 32, 64, 128 */
+  KDA_ERR_CONFIG = 10     /* rows_per_workgroup not 0, 16, 32 or 64, or segment_chunks
+                             above 2^24 */
 } kda_status;
 
 enum {
@@ -112,29 +113,53 @@ typedef struct kda_prefill_args {
   uint32_t flags;        /* KDA_FLAG_* */
 
   /* Launch geometry: value rows handled by one workgroup of the recurrence (each
-     wave owns 16 rows). 0 = automatic (fill the compute units); 16/32/64/128 force it.
-     Results are bitwise identical for every choice. */
+     compute wave owns 16 rows). 0 = automatic; 16/32/64 force it. For a given
+     segment_chunks, results are bitwise identical for every choice. */
   int32_t rows_per_workgroup;
+
+  /* Time segments of the recurrence. The chunk-to-chunk carry is affine in the state,
+     so a sequence can be cut into segments of this many chunks that run in parallel:
+     each middle segment's transition (128 x 128) and zero-start end state are computed
+     first, the segment start states are then combined serially (one 128x128x128
+     product per segment), and every segment is re-run from its true start to produce
+     o. It trades about three times the recurrence work for a critical path of about
+     two segments, which pays off when few (sequence, head) pairs leave compute units
+     idle. 0 = automatic (segments only when N * H <= 32, sized so the first pass has
+     about one workgroup per compute unit of a 256-CU device); negative = never (one
+     serial run per sequence); positive = this many chunks per segment. Results differ
+     from the serial form only by rounding. */
+  int32_t segment_chunks;
 
   /* Optional timing hooks (host array of hipEvent_t handles, or NULL). When
      n_trace_events >= 3, the library records trace_events[0] before the first kernel,
      trace_events[1] between the preparation and recurrence kernels and
-     trace_events[2] after the recurrence kernel, all on the call's stream. */
+     trace_events[2] after the last recurrence kernel, all on the call's stream. When
+     n_trace_events >= 5 it also records trace_events[3] after the first recurrence
+     launch and trace_events[4] after the segment combine (both right after the
+     recurrence in the serial form). */
   void *const *trace_events;
   int32_t n_trace_events;
 } kda_prefill_args;
 
 /*
- * Workspace layout (bytes, from the workspace base):
- *   [0, KDA_WS_HEADER)            int64 cu_chunks[N + 1] (varlen only): exclusive prefix
- *                                 of ceil(len_n / 16) (the flashinfer page's compact
- *                                 chunk prefix, section "Packed scheduling").
+ * Workspace layout (bytes, from the workspace base; kda_prefill_plan reports the
+ * offsets):
+ *   [0, KDA_WS_HEADER)            varlen only: int64 cu_chunks[N + 1], the exclusive
+ *                                 prefix of ceil(len_n / 16) (the flashinfer page's
+ *                                 compact chunk prefix, section "Packed scheduling"),
+ *                                 then int64 cu_segs[N + 1], the prefix of the segment
+ *                                 counts max(1, ceil(chunks_n / segment_chunks)).
  *   [KDA_WS_HEADER, ...)          one KDA_WS_RECORD-byte record per (chunk c, head h)
  *                                 at index h * max_chunks + c, where c counts chunks
  *                                 over all sequences in order and max_chunks is the
  *                                 plan's bound (kda_prefill_plan): N * ceil(T / 16)
  *                                 for the fixed layout, (T + 15 N) / 16 for varlen.
- * KDA_WS_HEADER = round_up((N + 1) * 8, 256).
+ *   scan_state_offset             segmented form only: FP32 [H][S][128][128], the
+ *                                 start state (or zero-start end state) per segment,
+ *                                 S = segments_per_head_bound.
+ *   scan_transition_offset        segmented form only: BF16 [H][S][128][128], each
+ *                                 middle segment's transition, stored transposed.
+ * KDA_WS_HEADER = round_up((N + 1) * 16, 256) for varlen, 0 for the fixed layout.
  *
  * A record holds, for the chunk's 16 tokens (pad tokens of a short last chunk behave as
  * k = q = v = 0, g = 0, beta = 0), with the page's K_start, Q_start, K_end, D_{0:15},
@@ -180,14 +205,22 @@ kda_status kda_debug_check_cu_seqlens(const int64_t *cu_seqlens, int64_t N, int6
                                       void *stream);
 
 /* Launch geometry the call would use (host only): recurrence rows per workgroup,
-   workgroup count of each kernel, and the upper bound on the chunk count. */
+   workgroup count of each kernel, the upper bound on the chunk count and the
+   segmented form's parameters. num_cus only affects the automatic row choice of the
+   serial form (0 = 256). */
 typedef struct kda_plan_info {
   int32_t rows_per_workgroup;
-  int32_t waves_per_workgroup;
-  int64_t recurrence_workgroups;
+  int32_t waves_per_workgroup;     /* compute + loader waves of a recurrence workgroup */
+  int64_t recurrence_workgroups;   /* serial launch, or the first segmented launch */
   int64_t prepare_workgroups;
   int64_t max_chunks;
   size_t workspace_header_bytes;
+  int64_t segment_chunks;          /* 0: serial form */
+  int64_t segments_per_head_bound; /* scan slots per head */
+  int64_t combine_workgroups;
+  int64_t scan_c_workgroups;       /* the re-run launch */
+  size_t scan_state_offset;
+  size_t scan_transition_offset;
 } kda_plan_info;
 kda_status kda_prefill_plan(const kda_prefill_args *a, int32_t num_cus, kda_plan_info *out);
 

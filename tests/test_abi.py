@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = kda.load_library()
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for code in range(11):
         assert kda.kda_status_string(code) and kda.kda_status_string(code) != "unknown status"
     assert kda.kda_status_string(99) == "unknown status"
@@ -126,7 +126,8 @@ def test_workspace_checks():
     assert status(fake(T=100, H=3, workspace_bytes=need - 1)) == 7
     assert status(fake(T=100, H=3, workspace=None)) == 7
     assert status(fake(T=100, H=3, workspace=0x7F0000000000 + 8 * 256 * MB + 128)) == 7
-    # varlen: (T + 15 N) / 16 chunk records plus the 256-byte-rounded cu_chunks header
+    # varlen: (T + 15 N) / 16 chunk records plus the 256-byte-rounded header
+    # (cu_chunks and cu_segs, 2 (N + 1) int64)
     v = fake(T=100, H=3, N=5, varlen=True)
     assert kda.kda_prefill_workspace_bytes(v) == 256 + ((100 + 15 * 5) // 16) * 3 * kda.KDA_WS_RECORD
 
@@ -144,6 +145,37 @@ def test_plan_follows_the_slice_rule():
     assert p["rows_per_workgroup"] == 64 and p["recurrence_workgroups"] == 192
     assert p["prepare_workgroups"] == 512 * 96
     assert kda.kda_prefill_plan(fake(H=6, rows_per_workgroup=64), 256)["recurrence_workgroups"] == 12
+    assert status(fake(rows_per_workgroup=128)) == 10
+    assert status(fake(rows_per_workgroup=48)) == 10
+
+
+def test_plan_segments_small_head_counts():
+    # H = 6, T = 8192: 512 chunks; P = (256 / 6 + 6) / 4 = 12 segments of 43 chunks.
+    p = kda.kda_prefill_plan(fake(H=6, T=8192), 256)
+    assert p["segment_chunks"] == 43 and p["segments_per_head_bound"] == 12
+    assert p["rows_per_workgroup"] == 64
+    assert p["recurrence_workgroups"] == 6 * 12 * 4     # 256-row space: Z and Phi rows
+    assert p["scan_c_workgroups"] == 6 * 12 * 2
+    assert p["combine_workgroups"] == 6 * 2
+    records = 512 * 6 * kda.KDA_WS_RECORD
+    assert p["scan_state_offset"] == records            # already 256-byte aligned
+    slots = 6 * 12
+    assert p["scan_transition_offset"] == records + slots * 128 * 128 * 4
+    need = kda.kda_prefill_workspace_bytes(fake(H=6, T=8192))
+    assert need == records + slots * 128 * 128 * 6
+    # Forced serial, forced length, and no segments for many heads.
+    s = kda.kda_prefill_plan(fake(H=6, T=8192, segment_chunks=-1), 256)
+    assert s["segment_chunks"] == 0 and s["rows_per_workgroup"] == 16
+    assert kda.kda_prefill_workspace_bytes(fake(H=6, T=8192, segment_chunks=-1)) == records
+    f = kda.kda_prefill_plan(fake(H=6, T=8192, segment_chunks=100), 256)
+    assert f["segment_chunks"] == 100 and f["segments_per_head_bound"] == 6
+    assert kda.kda_prefill_plan(fake(H=96, T=8192), 256)["segment_chunks"] == 0
+    # Varlen: slots bound = ceil(max_chunks / L) + N.
+    v = kda.kda_prefill_plan(fake(H=2, T=4000, N=3, varlen=True, segment_chunks=20), 256)
+    mc = (4000 + 15 * 3) // 16
+    assert v["segments_per_head_bound"] == (mc + 19) // 20 + 3
+    assert v["workspace_header_bytes"] == 256
+    assert status(fake(segment_chunks=1 << 25)) == 10
 
 
 def test_last_error_explains_rejection():
