@@ -99,8 +99,9 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def make_call(x, device):
-    """Device inputs, outputs and workspace for one configuration (allocated once)."""
+def make_call(x, device, **extra):
+    """Device inputs, outputs and workspace for one configuration (allocated once).
+    extra: further kda_prefill keyword arguments (launch geometry)."""
     import torch
 
     import chunkwise_delta_rule_kda_amd as kda
@@ -109,7 +110,7 @@ def make_call(x, device):
     d = to_device(x, device)
     o = torch.empty_like(d["v"])
     st = torch.empty((x.N, x.H, D, D), dtype=d["state_dtype"], device=device)
-    args = kda.make_args(B=x.B, T=x.T, H=x.H, N=x.N, cu_seqlens=d.get("cu_seqlens"))
+    args = kda.make_args(B=x.B, T=x.T, H=x.H, N=x.N, cu_seqlens=d.get("cu_seqlens"), **extra)
     ws = torch.empty(kda.kda_prefill_workspace_bytes(args), dtype=torch.uint8, device=device)
 
     def call(trace=None):
@@ -118,34 +119,42 @@ def make_call(x, device):
                         dt_bias=d.get("dt_bias"), lower_bound=d.get("lower_bound"),
                         l2norm_qk=x.l2norm_qk, beta_is_logit=x.beta_is_logit,
                         state_dtype=d["state_dtype"], o=o, state_out=st, workspace=ws,
-                        trace_events=trace)
+                        trace_events=trace, **extra)
 
     return call, (o, st)
 
 
-def time_config(x, steps, warmup, device, hip):
+def time_config(x, steps, warmup, device, hip, **extra):
     import torch
 
-    call, _ = make_call(x, device)
+    call, _ = make_call(x, device, **extra)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    evs = hip.create(3 * steps)
+    # Events per step: start, after prepare, after the last recurrence launch, after
+    # the first recurrence launch, after the segment combine (see kda.h).
+    E = 5
+    evs = hip.create(E * steps)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
     for i in range(steps):
-        call(trace=evs[3 * i:3 * i + 3])
+        call(trace=evs[E * i:E * i + E])
     stop.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
-    prep = [hip.elapsed_ms(evs[3 * i], evs[3 * i + 1]) for i in range(steps)]
-    rec = [hip.elapsed_ms(evs[3 * i + 1], evs[3 * i + 2]) for i in range(steps)]
+    ev = lambda i, j: evs[E * i + j]
+    prep = [hip.elapsed_ms(ev(i, 0), ev(i, 1)) for i in range(steps)]
+    rec = [hip.elapsed_ms(ev(i, 1), ev(i, 2)) for i in range(steps)]
+    rec_a = [hip.elapsed_ms(ev(i, 1), ev(i, 3)) for i in range(steps)]
+    comb = [hip.elapsed_ms(ev(i, 3), ev(i, 4)) for i in range(steps)]
+    rec_c = [hip.elapsed_ms(ev(i, 4), ev(i, 2)) for i in range(steps)]
     hip.destroy(evs)
-    return dict(ms_per_step=total_ms / steps, wall_s=t_wall, prep_ms=prep, rec_ms=rec)
+    return dict(ms_per_step=total_ms / steps, wall_s=t_wall, prep_ms=prep, rec_ms=rec,
+                rec_a_ms=rec_a, combine_ms=comb, rec_c_ms=rec_c)
 
 
 def cpu_baseline(x, budget_s=10.0, max_reps=30):
@@ -195,6 +204,10 @@ def summarize(x, r):
         mfma_frac=round(alg_flop / (tot_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 5),
         link_ns=round(rec_us * 1e3 / max(1, (x.T + C - 1) // C), 1) if x.cu_seqlens is None
         else None,
+        recurrence_phases_us=dict(
+            first=round(statistics.mean(r["rec_a_ms"]) * 1e3, 2),
+            combine=round(statistics.mean(r["combine_ms"]) * 1e3, 2),
+            rerun=round(statistics.mean(r["rec_c_ms"]) * 1e3, 2)),
     )
 
 

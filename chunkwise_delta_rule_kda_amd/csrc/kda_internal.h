@@ -9,12 +9,11 @@ namespace kda {
 constexpr int kD = 128;          // head dimension (keys = values = 128)
 constexpr int kC = 16;           // tokens per chunk
 constexpr int kRecord = 13824;   // bytes of one prepared (chunk, head) record
-constexpr int kOffKn = 0;        // bf16 [4][64][8]
-constexpr int kOffQt = 4096;     // bf16 [4][64][8]
-constexpr int kOffKeT = 8192;    // bf16 [8][64][4]
-constexpr int kOffD = 12288;     // fp32 [128]
-constexpr int kOffMb = 12800;    // bf16 [64][4]
-constexpr int kOffAqk = 13312;   // bf16 [64][4]
+constexpr int kOffKn = 0;        // bf16 [kb 4][L 64][e 8]
+constexpr int kOffQt = 4096;     // bf16 [kb 4][L 64][e 8]
+constexpr int kOffKeT = 8192;    // bf16 [bp 4][L 64][half 2][j 4]
+constexpr int kOffD = 12288;     // fp32 [L 64][2] (row-broadcast order)
+constexpr int kOffMbAq = 12800;  // bf16 [L 64][Mb 4, A_qk 4]
 
 // Recurrence launch modes: one serial run per sequence, or the launches of the
 // segmented (time-parallel) form.

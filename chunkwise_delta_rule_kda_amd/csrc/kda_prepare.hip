@@ -194,15 +194,19 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
   *reinterpret_cast<u32x4*>(&sKi[r][cq]) = *reinterpret_cast<const u32x4*>(bki);
   *reinterpret_cast<u32x4*>(&sKe[r][cq]) = *reinterpret_cast<const u32x4*>(bke);
   if (r == 0) {
-    f32x4 d0, d1;
+    // D_{0:15}, ordered for a row broadcast: lane L = 16 g + m holds the pair of keys
+    // 16 (m / 2) + 4 g + 2 (m % 2) + {0, 1}, so that the 16 lanes of row g together hold
+    // the 32 keys 16 b + 4 g + j that each of them needs.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      d0[e] = __expf(G15[e]);
-      d1[e] = __expf(G15[4 + e]);
+    for (int e = 0; e < 8; e += 2) {
+      const int key = cq + e;
+      const int b = key >> 4, g = (key >> 2) & 3, hh = (key >> 1) & 1;
+      const int L = 16 * g + 2 * b + hh;
+      f32x2 v;
+      v[0] = __expf(G15[e]);
+      v[1] = __expf(G15[e + 1]);
+      *reinterpret_cast<f32x2*>(rec + kOffD + L * 8) = v;
     }
-    f32x4* dst = reinterpret_cast<f32x4*>(rec + kOffD + cq * 4);
-    dst[0] = d0;
-    dst[1] = d1;
   }
   __syncthreads();
 
@@ -231,18 +235,16 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
     }
   }
   {
-    // K_end^T record, [b 8][L 64][j 4] = K_end[4 grp(L) + j][16 b + m(L)]; 8 elements
-    // (two lanes) per thread.
-    const int f0 = 8 * tid;
-    const int b = f0 >> 8;
-    const int L0 = (f0 >> 2) & 63;
+    // K_end^T record, [bp 4][L 64][half 2][j 4] = K_end[4 grp(L) + j][16 (2 bp + half) +
+    // m(L)]: one 16-byte piece per (block pair, lane), one per thread.
+    const int bp = tid >> 6;
+    const int L = tid & 63;
     unsigned short out[8];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int L = L0 + half;
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[4 * half + j] = sKe[4 * (L >> 4) + j][16 * b + (L & 15)];
-    }
+      for (int j = 0; j < 4; ++j)
+        out[4 * half + j] = sKe[4 * (L >> 4) + j][16 * (2 * bp + half) + (L & 15)];
     *reinterpret_cast<u32x4*>(rec + kOffKeT + 16 * tid) = *reinterpret_cast<const u32x4*>(out);
   }
   __syncthreads();
@@ -273,15 +275,16 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
     for (int i = 0; i < kC; ++i) P += sA[mi][i] * sM[i][c];
     sNP[mi][c] = float_to_bf16_bits(-P);
     sNM[mi][c] = float_to_bf16_bits(-sM[mi][c]);
-    if (tid < 128) {
-      const int L = tid & 63;
+    if (tid < 64) {  // [L 64][Mb j 4, A_qk j 4]
+      const int L = tid;
       const int mm = L & 15, g2 = L >> 4;
-      unsigned short out[4];
+      unsigned short out[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        out[j] = float_to_bf16_bits(tid < 64 ? sM[mm][4 * g2 + j] : sA[mm][4 * g2 + j]);
-      *reinterpret_cast<u32x2*>(rec + (tid < 64 ? kOffMb : kOffAqk) + 8 * L) =
-          *reinterpret_cast<const u32x2*>(out);
+      for (int j = 0; j < 4; ++j) {
+        out[j] = float_to_bf16_bits(sM[mm][4 * g2 + j]);
+        out[4 + j] = float_to_bf16_bits(sA[mm][4 * g2 + j]);
+      }
+      *reinterpret_cast<u32x4*>(rec + kOffMbAq + 16 * L) = *reinterpret_cast<const u32x4*>(out);
     }
   }
   __syncthreads();

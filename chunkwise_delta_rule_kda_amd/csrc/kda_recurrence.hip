@@ -42,9 +42,9 @@
 // Ring protocol, iteration c:
 //   loaders: write chunk c+1 into slot (c+1)%3, issue the loads of chunk c+1+DEPTH,
 //            wait for their own LDS writes, barrier B_c;
-//   compute: read chunk c's tail operands (slot c%3), store the O of chunk c-1, wait
-//            for own LDS reads, barrier B_c, read chunk c+1's chain operands, compute c.
-// Slot (c+1)%3 last held chunk c-2, whose final reads happened before B_{c-2}; the
+//   compute: barrier B_c, read all of chunk c+1's operands (slot (c+1)%3), compute c
+//            (operands read in the previous iteration), store the O of chunk c-1.
+// Slot (c+1)%3 last held chunk c-2, whose reads were consumed before B_{c-2}; the
 // loaders write it after B_{c-1}.
 
 #include "kda_device.h"
@@ -66,6 +66,15 @@ __device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMI
 __device__ __forceinline__ void lds_barrier() {
   compiler_fence();
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// Meet the other waves without waiting for this wave's own LDS reads (a wave that only
+// reads LDS: every read it issues is consumed, and so complete, before the wave reaches
+// the barrier after next, the first after which that slot is rewritten).
+__device__ __forceinline__ void read_barrier() {
+  compiler_fence();
   __builtin_amdgcn_s_barrier();
   compiler_fence();
 }
@@ -243,17 +252,17 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
   return true;
 }
 
-struct ChainIn {  // needed at the very start of a chunk (read one chunk ahead)
+struct ChainIn {  // operands of the chunk's first products
   bf16x8 kn[4];
   i16x4 mb;
+  i16x4 aq;
   i16x4 vv;
 };
 
-struct TailIn {  // needed later in the chunk (read at its start)
-  i16x4 ke[8];
-  f32x4 d[8];
+struct TailIn {  // operands of the state update and the output
+  u32x4 ke[4];  // K_end^T blocks 2 bp and 2 bp + 1 (8 bytes each)
+  f32x2 dv;     // this lane's pair of D_{0:15} entries (row-broadcast order)
   bf16x8 qt[4];
-  i16x4 aq;
 };
 
 template <bool BF16IO, int W>
@@ -266,8 +275,10 @@ __device__ __forceinline__ void read_chain(ChainIn& x, const lds_u8* slot, int l
   for (int kb = 0; kb < 4; ++kb)
     x.kn[kb] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
         slot + kOffKn + kb * 1024 + lane * 16);
-  x.mb = *reinterpret_cast<const __attribute__((address_space(3))) i16x4*>(slot + kOffMb +
-                                                                          lane * 8);
+  const u32x4 ma =
+      *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(slot + kOffMbAq + lane * 16);
+  x.mb = __builtin_bit_cast(i16x4, u32x2{ma[0], ma[1]});
+  x.aq = __builtin_bit_cast(i16x4, u32x2{ma[2], ma[3]});
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tok = 4 * grp + j;
@@ -283,20 +294,45 @@ __device__ __forceinline__ void read_chain(ChainIn& x, const lds_u8* slot, int l
 }
 
 __device__ __forceinline__ void read_tail(TailIn& x, const lds_u8* slot, int lane) {
-  const int grp = lane >> 4;
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    x.ke[b] = *reinterpret_cast<const __attribute__((address_space(3))) i16x4*>(
-        slot + kOffKeT + b * 512 + lane * 8);
-    x.d[b] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-        slot + kOffD + (16 * b + 4 * grp) * 4);
-  }
+  for (int bp = 0; bp < 4; ++bp)
+    x.ke[bp] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+        slot + kOffKeT + bp * 1024 + lane * 16);
+  x.dv = *reinterpret_cast<const __attribute__((address_space(3))) f32x2*>(slot + kOffD + lane * 8);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
     x.qt[kb] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
         slot + kOffQt + kb * 1024 + lane * 16);
-  x.aq = *reinterpret_cast<const __attribute__((address_space(3))) i16x4*>(slot + kOffAqk +
-                                                                          lane * 8);
+}
+
+// Lane N of this lane's 16-lane row (DPP row broadcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
+}
+
+// State block B (keys 16 B + 4 grp + j) times D: key 16 B + 4 grp + j sits in lane
+// 2 B + j / 2 of the row, component j % 2.
+template <int B>
+__device__ __forceinline__ f32x4 decayed(f32x4 st, f32x2 dv) {
+  f32x4 r;
+  r[0] = st[0] * row_bcast<2 * B>(dv[0]);
+  r[1] = st[1] * row_bcast<2 * B>(dv[1]);
+  r[2] = st[2] * row_bcast<2 * B + 1>(dv[0]);
+  r[3] = st[3] * row_bcast<2 * B + 1>(dv[1]);
+  return r;
+}
+
+// S^T block B <- D (.) S^T + K_end^T U^T for B = I .. 7.
+template <int I>
+__device__ __forceinline__ void state_update(f32x4 (&st)[8], const TailIn& b, i16x4 up) {
+  if constexpr (I < 8) {
+    const u32x4 kp = b.ke[I / 2];
+    const i16x4 ke = __builtin_bit_cast(i16x4, (I % 2) ? u32x2{kp[2], kp[3]} : u32x2{kp[0], kp[1]});
+    st[I] = mfma16(ke, up, decayed<I>(st[I], b.dv));
+    state_update<I + 1>(st, b, up);
+  }
 }
 
 // One chunk for one wave: updates the state and returns O[value 4 grp + j][token m].
@@ -313,8 +349,7 @@ __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f
   u += uv;
   const i16x4 up = pack4(u);
   const bf16x8 s0 = sp[0], s1 = sp[1], s2 = sp[2], s3 = sp[3];  // entering state
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st[i] = mfma16(b.ke[i], up, st[i] * b.d[i]);
+  state_update<0>(st, b, up);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) sp[kb] = pack8(st[2 * kb], st[2 * kb + 1]);
   // O from the entering state (off the chain)
@@ -322,7 +357,7 @@ __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f
   out = mfma32(s1, b.qt[1], out);
   out = mfma32(s2, b.qt[2], out);
   out = mfma32(s3, b.qt[3], out);
-  out += mfma16(pack4(uv), b.aq, zero);
+  out += mfma16(pack4(uv), a.aq, zero);
   return out;
 }
 
@@ -342,9 +377,12 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
                             (t.tok0 * p.H * kD + t.h * kD + vcol) * T::ES;
   const int64_t vchunk_b = kC * vstride_b;
   const int64_t nch = t.nch;
-  // Per-unit source offsets that do not depend on the chunk.
-  int64_t off[T::K];
-  int vtok[T::K];  // V token row of the unit, or -1 for a record unit
+  // Per-unit source address of chunk 0 and its step per chunk. A V unit of a pad token
+  // (past the sequence end, only in a sequence's last chunk) reads token row 0 instead.
+  const unsigned char* base[T::K];
+  uint32_t inc[T::K];
+  int vtok[T::K];       // V token row of the unit, or -1 for a record unit
+  int64_t vdrop[T::K];  // bytes back to token row 0 for a V unit
 #pragma unroll
   for (int k = 0; k < T::K; ++k) {
     const int u = lt + k * T::LT;
@@ -352,26 +390,31 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
     if (i >= 0 && i < T::VROW && !t.vzero) {
       const int tok = i / T::PARTS;
       vtok[k] = tok;
-      off[k] = (i - tok * T::PARTS) * 16;
+      vdrop[k] = tok * vstride_b;
+      base[k] = v0 + tok * vstride_b + (i - tok * T::PARTS) * 16;
+      inc[k] = static_cast<uint32_t>(vchunk_b);
     } else {
       vtok[k] = -1;
-      off[k] = u < kRecUnits ? u * 16 : 0;
+      vdrop[k] = 0;
+      base[k] = rec0 + (u < kRecUnits ? u * 16 : 0);
+      inc[k] = kRecord;
     }
   }
   u32x4 r[T::DEPTH][T::K];
   auto issue = [&](u32x4(&dst)[T::K], int64_t j) {
     j = j < nch - 1 ? j : nch - 1;
-    const unsigned char* rec = rec0 + j * kRecord;
-    const unsigned char* vt = v0 + j * vchunk_b;
     const int64_t nvalid = t.tok_end - (t.tok0 + j * kC);
+    if (nvalid >= kC) {
 #pragma unroll
-    for (int k = 0; k < T::K; ++k) {
-      const unsigned char* src;
-      if (vtok[k] >= 0)
-        src = vt + (vtok[k] < nvalid ? vtok[k] : 0) * vstride_b + off[k];  // pad rows: row 0
-      else
-        src = rec + off[k];
-      dst[k] = *reinterpret_cast<const u32x4*>(src);
+      for (int k = 0; k < T::K; ++k)
+        dst[k] = *reinterpret_cast<const u32x4*>(base[k] + static_cast<uint64_t>(j) * inc[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < T::K; ++k) {
+        const unsigned char* src = base[k] + static_cast<uint64_t>(j) * inc[k];
+        if (vtok[k] >= nvalid) src -= vdrop[k];
+        dst[k] = *reinterpret_cast<const u32x4*>(src);
+      }
     }
   };
   auto put = [&](const u32x4(&src)[T::K], int slot) {
@@ -449,33 +492,46 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
     return t.vzero ? 0 : t.tok_end - (t.tok0 + c * kC);
   };
   if (nch > 0) {
-    lds_barrier();  // B_{-1}: chunk 0 visible
+    read_barrier();  // B_{-1}: chunk 0 visible
     ChainIn cur;
     read_chain<BF16IO, W>(cur, ring, lane, wave, nvalid_of(0));
     int cs = 0;  // slot of chunk c
-    // O of chunk c is stored at the start of iteration c + 1, before the barrier: loads
-    // and stores retire through one in-order counter, so a later wait for this wave's
-    // loads never waits for this store.
+    // The O of chunk c is stored in iteration c + 1, after that iteration's MFMA work
+    // has been issued, so that its wait for chunk c's last products is hidden.
     f32x4 pend = {0.f, 0.f, 0.f, 0.f};
     const int64_t obase = t.tok0 * vstride + t.h * kD + v0;
-    auto store_out = [&](int64_t c) {
+    auto store_out = [&](int64_t c, f32x4 val) {
       if (m < t.tok_end - (t.tok0 + c * kC))
-        store4<BF16IO>(p.o, obase + (c * kC + m) * vstride + 4 * grp, pend);
+        store4<BF16IO>(p.o, obase + (c * kC + m) * vstride + 4 * grp, val);
     };
+    TailIn tail;
+    read_tail(tail, ring, lane);
 #pragma unroll 1
     for (int64_t c = 0; c < nch; ++c) {
       const int ns = cs + 1 == kSlots ? 0 : cs + 1;  // slot of chunk c + 1
-      TailIn tail;
-      read_tail(tail, ring + cs * T::SLOT, lane);
-      if (t.out && c > 0) store_out(c - 1);
-      lds_barrier();  // B_c: chunk c + 1 visible
+      read_barrier();  // B_c: chunk c + 1 visible
+      // All of chunk c + 1's operands are read here, one chunk ahead, so that their
+      // latency (they queue behind the loaders' writes of chunk c + 2) is hidden by
+      // chunk c's MFMA work.
       ChainIn nxt;
+      TailIn ntail;
       read_chain<BF16IO, W>(nxt, ring + ns * T::SLOT, lane, wave, nvalid_of(c + 1));
+      read_tail(ntail, ring + ns * T::SLOT, lane);
+      const f32x4 prev = pend;
       pend = chunk_step(cur, tail, st, sp);
+      if (t.out && c > 0) store_out(c - 1, prev);
+      // Keep the reads in this iteration: without these uses the compiler sinks them to
+      // the top of the next iteration, right before the MFMA chain that needs them.
+      asm volatile("" ::"v"(nxt.kn[0]), "v"(nxt.kn[1]), "v"(nxt.kn[2]), "v"(nxt.kn[3]),
+                   "v"(nxt.mb), "v"(nxt.aq), "v"(nxt.vv));
+      asm volatile("" ::"v"(ntail.ke[0]), "v"(ntail.ke[1]), "v"(ntail.ke[2]), "v"(ntail.ke[3]),
+                   "v"(ntail.dv), "v"(ntail.qt[0]), "v"(ntail.qt[1]), "v"(ntail.qt[2]),
+                   "v"(ntail.qt[3]));
       cur = nxt;
+      tail = ntail;
       cs = ns;
     }
-    if (t.out) store_out(nch - 1);
+    if (t.out) store_out(nch - 1, pend);
   }
 
   if (t.final_state && p.state_out) {
@@ -496,7 +552,9 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
 }
 
 template <bool BF16IO, bool BF16ST, int W>
-__global__ __launch_bounds__(block_threads(W)) void kda_recurrence_kernel(Params p) {
+// At most two waves per SIMD (256 registers each): with more room the compiler keeps
+// the state in AGPRs and copies it through VGPRs every chunk for the decay multiply.
+__global__ __launch_bounds__(block_threads(W), 2) void kda_recurrence_kernel(Params p) {
   using T = Tile<BF16IO, W>;
   static_assert(T::NT == block_threads(W), "block size");
   __shared__ __attribute__((aligned(16))) unsigned char ring_[kSlots * T::SLOT];

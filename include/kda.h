@@ -171,12 +171,14 @@ typedef struct kda_prefill_args {
  * O^T = Qt S^T + A_qk Mb V^T and S_next^T = D_{0:15} S^T + K_end^T U^T.
  * Offsets inside a record (tok m, lane L = 16 * grp + m, key index
  * kappa(kb, grp, e) = 32 kb + 16 (e / 4) + 4 grp + (e % 4)):
- *   0      bf16 Kn [kb 4][L 64][e 8]  = Kn[m][kappa(kb, grp, e)]
- *   4096   bf16 Qt [kb 4][L 64][e 8]  = Qt[m][kappa(kb, grp, e)]
- *   8192   bf16 KeT[b 8][L 64][j 4]   = K_end[4 grp + j][16 b + m]
- *   12288  fp32 D  [128]              = D_{0:15}[key]
- *   12800  bf16 Mb [L 64][j 4]        = Mb[m][4 grp + j]
- *   13312  bf16 Aqk[L 64][j 4]        = A_qk[m][4 grp + j]
+ *   0      bf16 Kn [kb 4][L 64][e 8]          = Kn[m][kappa(kb, grp, e)]
+ *   4096   bf16 Qt [kb 4][L 64][e 8]          = Qt[m][kappa(kb, grp, e)]
+ *   8192   bf16 KeT[bp 4][L 64][h 2][j 4]     = K_end[4 grp + j][16 (2 bp + h) + m]
+ *   12288  fp32 D  [L 64][c 2]                = D_{0:15}[16 (m / 2) + 4 grp + 2 (m % 2) + c]
+ *   12800  bf16 MA [L 64][Mb j 4, A_qk j 4]   = Mb[m][4 grp + j], A_qk[m][4 grp + j]
+ * (each lane's operands are one contiguous 8- or 16-byte piece; D is ordered so that
+ * the 16 lanes of a row hold the 32 entries each of them needs, exchanged by a row
+ * broadcast).
  */
 #define KDA_WS_RECORD 13824
 

@@ -40,6 +40,11 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name)
 
 
+def test_record_size_matches_header():
+    m = re.search(r"#define KDA_WS_RECORD (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == kda.KDA_WS_RECORD
+
+
 def test_abi_version_and_status_strings():
     lib = kda.load_library()
     assert lib.kda_abi_version() == 2

@@ -29,25 +29,27 @@ def decode(rec):
     u16 = rec.view(np.uint16)
     kn = bf16_bits_to_f32(u16[0:2048]).reshape(4, 64, 8)
     qt = bf16_bits_to_f32(u16[2048:4096]).reshape(4, 64, 8)
-    ke = bf16_bits_to_f32(u16[4096:6144]).reshape(8, 64, 4)
-    D = rec[12288:12800].view(np.float32)
-    mb = bf16_bits_to_f32(u16[6400:6656]).reshape(64, 4)
-    aq = bf16_bits_to_f32(u16[6656:6912]).reshape(64, 4)
+    ke = bf16_bits_to_f32(u16[4096:6144]).reshape(4, 64, 2, 4)
+    D = rec[12288:12800].view(np.float32).reshape(64, 2)
+    ma = bf16_bits_to_f32(u16[6400:6912]).reshape(64, 2, 4)
     Kn = np.zeros((16, 128)); Qt = np.zeros((16, 128)); Ke = np.zeros((16, 128))
-    M = np.zeros((16, 16)); A = np.zeros((16, 16))
+    M = np.zeros((16, 16)); A = np.zeros((16, 16)); Dn = np.zeros(128)
     for L in range(64):
         m, grp = L % 16, L // 16
         for kb in range(4):
             for e in range(8):
                 Kn[m, kappa(kb, grp, e)] = kn[kb, L, e]
                 Qt[m, kappa(kb, grp, e)] = qt[kb, L, e]
-        for b in range(8):
-            for j in range(4):
-                Ke[4 * grp + j, 16 * b + m] = ke[b, L, j]
+        for bp in range(4):
+            for h in range(2):
+                for j in range(4):
+                    Ke[4 * grp + j, 16 * (2 * bp + h) + m] = ke[bp, L, h, j]
+        for c in range(2):
+            Dn[16 * (m // 2) + 4 * grp + 2 * (m % 2) + c] = D[L, c]
         for j in range(4):
-            M[m, 4 * grp + j] = mb[L, j]
-            A[m, 4 * grp + j] = aq[L, j]
-    return dict(Kn=Kn, Qt=Qt, K_end=Ke, D=D.astype(np.float64), Mb=M, A_qk=A)
+            M[m, 4 * grp + j] = ma[L, 0, j]
+            A[m, 4 * grp + j] = ma[L, 1, j]
+    return dict(Kn=Kn, Qt=Qt, K_end=Ke, D=Dn, Mb=M, A_qk=A)
 
 
 def expected(q, k, g, beta, s):
@@ -79,7 +81,7 @@ def run_and_check(x, chunks_to_check=None, tols=TOLS):
     kda.kda_prefill(q, k, v, g, beta, workspace=ws, **d)
     torch.cuda.synchronize()
     wsn = ws.cpu().numpy()
-    header = 0 if x.cu_seqlens is None else ((x.N + 1) * 8 + 255) // 256 * 256
+    header = kda.kda_prefill_plan(args)["workspace_header_bytes"]
     max_chunks = (x.N * ((x.T + 15) // 16) if x.cu_seqlens is None
                   else (x.T + 15 * x.N) // 16)
     # Oracle-side inputs after the in-kernel transforms (FP64).
