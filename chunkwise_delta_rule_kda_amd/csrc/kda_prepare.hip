@@ -69,32 +69,40 @@ __global__ __launch_bounds__(256) void kda_plan_kernel(const int64_t* __restrict
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
-  // fp32 tiles [token][channel]; sG is reused for Kn and sQf ends up holding Qt.
-  __shared__ __attribute__((aligned(16))) float sG[kC][kD];
-  __shared__ __attribute__((aligned(16))) float sQf[kC][kD];
-  // bf16 tiles [token][channel]
-  __shared__ __attribute__((aligned(16))) unsigned short sKs[kC][kD];
-  __shared__ __attribute__((aligned(16))) unsigned short sQs[kC][kD];
-  __shared__ __attribute__((aligned(16))) unsigned short sKi[kC][kD];
-  __shared__ __attribute__((aligned(16))) unsigned short sKe[kC][kD];
-  __shared__ float sBeta[kC];
-  __shared__ float sR[kC][kC + 1];
-  __shared__ float sA[kC][kC + 1];
-  __shared__ float sM[kC][kC + 1];
-  __shared__ __attribute__((aligned(16))) unsigned short sNM[kC][kC];
-  __shared__ __attribute__((aligned(16))) unsigned short sNP[kC][kC];
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations, not for its
+// global stores (the record stores are never read back by this kernel, and waiting for
+// them at every barrier would add an HBM write round trip each time).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
-  const int tid = threadIdx.x;
-  const int64_t gc = blockIdx.x;
-  const int64_t h = blockIdx.y;
-  const int64_t H = p.H;
+// DPP within 16-lane rows: lane r receives lane r - N of its row (0 past the row start),
+// or lane N of its row.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
+}
 
-  int64_t tok0, valid;
+// Token range of chunk gc (over all sequences, in order): first token and the number
+// of real tokens (0..16). False past the last chunk (varlen: the plan's count).
+struct ChunkSpan {
+  int64_t tok0;
+  int64_t valid;
+};
+
+__device__ __forceinline__ bool chunk_span(const Params& p, int64_t gc, ChunkSpan& sp) {
   if (p.cu_seqlens) {
     const int64_t total = p.cu_chunks[p.N];
-    if (gc >= total) return;  // uniform over the workgroup
+    if (gc >= total) return false;
     int64_t lo = 0, hi = p.N;  // first index with cu_chunks[idx] > gc
     while (lo < hi) {
       const int64_t mid = (lo + hi) >> 1;
@@ -102,43 +110,129 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
     }
     const int64_t s = lo > 0 ? lo - 1 : 0;
     const int64_t end = min(p.cu_seqlens[s + 1], p.T);
-    tok0 = p.cu_seqlens[s] + kC * (gc - p.cu_chunks[s]);
-    valid = min<int64_t>(kC, end - tok0);
+    sp.tok0 = p.cu_seqlens[s] + kC * (gc - p.cu_chunks[s]);
+    sp.valid = min<int64_t>(kC, end - sp.tok0);
   } else {
     const int64_t s = gc / p.chunks_per_seq;
     const int64_t lc = gc - s * p.chunks_per_seq;
-    tok0 = s * p.T + kC * lc;
-    valid = min<int64_t>(kC, p.T - kC * lc);
+    sp.tok0 = s * p.T + kC * lc;
+    sp.valid = min<int64_t>(kC, p.T - kC * lc);
   }
-  if (tok0 < 0) valid = 0;
-  unsigned char* rec = p.records + (h * p.max_chunks + gc) * (int64_t)kRecord;
+  if (sp.tok0 < 0) sp.valid = 0;
+  return true;
+}
 
-  // ---- load the chunk's rows and apply the optional transforms -------------------
-  const int r = tid >> 4;         // token of the chunk
-  const int cq = (tid & 15) * 8;  // first of this thread's 8 channels
-  const bool tv = r < valid;
-  const int64_t row = (tok0 + r) * H + h;
-  float q[8], k[8], g[8];
-  if (tv) {
-    load8<BF16>(p.q, row * kD + cq, q);
-    load8<BF16>(p.k, row * kD + cq, k);
-    load8<BF16>(p.g, row * kD + cq, g);
+// 8 consecutive elements of one row as loaded (BF16: one 16-byte piece; FP32: two).
+template <bool BF16>
+struct RawRow {
+  u32x4 w[BF16 ? 1 : 2];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void to_float(const RawRow<BF16>& x, float* out) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(x.w[0][i] << 16);
+      out[2 * i + 1] = __uint_as_float(x.w[0][i] & 0xffff0000u);
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = k[e] = g[e] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      out[i] = __uint_as_float(x.w[0][i]);
+      out[4 + i] = __uint_as_float(x.w[1][i]);
+    }
   }
-  if (p.flags & kFlagL2) {
+}
+
+// This thread's q, k, g pieces (token r, channels cq .. cq + 7) of a chunk, zeros past its
+// valid tokens; beta of token tid for tid < 16.
+template <bool BF16>
+__device__ __forceinline__ void load_rows(const Params& p, const ChunkSpan& sp, int64_t h, int r,
+                                          int cq, int tid, RawRow<BF16>& q, RawRow<BF16>& k,
+                                          RawRow<BF16>& g, float& beta) {
+  constexpr int ES = BF16 ? 2 : 4;
+  if (r < sp.valid) {
+    const int64_t off = (((sp.tok0 + r) * p.H + h) * kD + cq) * ES;
+#pragma unroll
+    for (int i = 0; i < (BF16 ? 1 : 2); ++i) {
+      q.w[i] = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(p.q) + off + 16 * i);
+      k.w[i] = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(p.k) + off + 16 * i);
+      g.w[i] = *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(p.g) + off + 16 * i);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < (BF16 ? 1 : 2); ++i) q.w[i] = k.w[i] = g.w[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  beta = 0.f;
+  if (tid < kC && tid < sp.valid) beta = load1<BF16>(p.beta, (sp.tok0 + tid) * p.H + h);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
+  // bf16 tiles [token][channel]: MFMA operands and the K_end^T record gather.
+  __shared__ __attribute__((aligned(16))) unsigned short sKs[kC][kD];  // K_start rows
+  __shared__ __attribute__((aligned(16))) unsigned short sQs[kC][kD];  // Q_start rows
+  __shared__ __attribute__((aligned(16))) unsigned short sKi[kC][kD];  // k / Gamma rows
+  __shared__ __attribute__((aligned(16))) unsigned short sKe[kC][kD];  // K_end rows
+  __shared__ __attribute__((aligned(16))) float sQf[kC][kD];           // s Q_start rows
+  __shared__ __attribute__((aligned(16))) float sR[kC][kC];
+  __shared__ __attribute__((aligned(16))) float sA[kC][kC];
+  __shared__ __attribute__((aligned(16))) float sM[kC][kC];
+  __shared__ __attribute__((aligned(16))) float sP[kC][kC];
+  __shared__ float sBeta[kC];
+  __shared__ float sNorm[2][4][kC];
+
+  const int tid = threadIdx.x;
+  const int64_t h = blockIdx.y;
+  const int64_t H = p.H;
+  // Thread (r, c8): token r = tid % 16, channels 8 c8 .. 8 c8 + 7, c8 = tid / 16, so the
+  // 16 tokens of a channel group form one 16-lane row (the prefix over tokens is a
+  // row scan).
+  const int r = tid & 15;
+  const int cq = (tid >> 4) * 8;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+
+  const int64_t gc = blockIdx.x;
+  ChunkSpan span;
+  if (!chunk_span(p, gc, span)) return;  // uniform over the workgroup
+  RawRow<BF16> rq, rk, rg;
+  float rbeta;
+  load_rows<BF16>(p, span, h, r, cq, tid, rq, rk, rg, rbeta);
+  const int64_t valid = span.valid;
+  unsigned char* rec = p.records + (h * p.max_chunks + gc) * (int64_t)kRecord;
+
+  // ---- this chunk's rows and the optional transforms -------------------------------
+  const bool tv = r < valid;
+  float q[8], k[8], g[8];
+  to_float<BF16>(rq, q);
+  to_float<BF16>(rk, k);
+  to_float<BF16>(rg, g);
+  if (tid < kC) {
+    float b = rbeta;
+    if ((p.flags & kFlagBetaLogit) && tid < valid) b = sigmoidf_(b);
+    sBeta[tid] = b;
+  }
+  if (p.flags & kFlagL2) {  // uniform branch
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sq += q[e] * q[e];
       sk += k[e] * k[e];
     }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-      sq += __shfl_xor(sq, off, 16);
-      sk += __shfl_xor(sk, off, 16);
+    // the 4 channel groups of this wave, then the 4 waves
+    sq += __shfl_xor(sq, 16);
+    sk += __shfl_xor(sk, 16);
+    sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 32);
+    if (lane < 16) {
+      sNorm[0][wave][r] = sq;
+      sNorm[1][wave][r] = sk;
     }
+    lds_barrier();
+    sq = sNorm[0][0][r] + sNorm[0][1][r] + sNorm[0][2][r] + sNorm[0][3][r];
+    sk = sNorm[1][0][r] + sNorm[1][1][r] + sNorm[1][2][r] + sNorm[1][3][r];
     const float iq = 1.0f / sqrtf(sq + 1e-6f);
     const float ik = 1.0f / sqrtf(sk + 1e-6f);
 #pragma unroll
@@ -153,27 +247,18 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
     for (int e = 0; e < 8; ++e)
       g[e] = p.lower_bound * sigmoidf_(a * (g[e] + p.dt_bias[h * kD + cq + e]));
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sG[r][cq + e] = g[e];
-  if ((tid & 15) == 0) {
-    float b = tv ? load1<BF16>(p.beta, row) : 0.f;
-    if ((p.flags & kFlagBetaLogit) && tv) b = sigmoidf_(b);
-    sBeta[r] = b;
-  }
-  __syncthreads();
 
-  // ---- prefix decay and the decayed key/query rows --------------------------------
+  // ---- prefix decay (row scan over tokens) and the decayed key/query rows ----------
   float G[8], G15[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) G[e] = G15[e] = 0.f;
-#pragma unroll
-  for (int t = 0; t < kC; ++t) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = sG[t][cq + e];
-      G15[e] += x;
-      if (t <= r) G[e] += x;
-    }
+  for (int e = 0; e < 8; ++e) {
+    float x = g[e];
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    G[e] = x;
+    G15[e] = row_bcast<15>(x);
   }
   unsigned short bks[8], bqs[8], bki[8], bke[8];
 #pragma unroll
@@ -200,19 +285,17 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const int key = cq + e;
-      const int b = key >> 4, g = (key >> 2) & 3, hh = (key >> 1) & 1;
-      const int L = 16 * g + 2 * b + hh;
+      const int b = key >> 4, gg = (key >> 2) & 3, hh = (key >> 1) & 1;
+      const int L = 16 * gg + 2 * b + hh;
       f32x2 v;
       v[0] = __expf(G15[e]);
       v[1] = __expf(G15[e + 1]);
       *reinterpret_cast<f32x2*>(rec + kOffD + L * 8) = v;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- R and A_qk on MFMA (waves 0, 1); K_end record (all threads) ----------------
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
   const int m = lane & 15;
   const int grp = lane >> 4;
   if (wave < 2) {
@@ -247,9 +330,9 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
         out[4 * half + j] = sKe[4 * (L >> 4) + j][16 * (2 * bp + half) + (L & 15)];
     *reinterpret_cast<u32x4*>(rec + kOffKeT + 16 * tid) = *reinterpret_cast<const u32x4*>(out);
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- A_kk = (I + R)^{-1} by forward substitution, one column per thread ----------
+  // ---- Mb = (I + R)^{-1} B by forward substitution, one column per thread ----------
   if (tid < kC) {
     const int c = tid;
     float x[kC];
@@ -257,78 +340,69 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
     for (int i = 0; i < kC; ++i) {
       float acc = i == c ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < i; ++j) acc -= sR[i][j] * x[j];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        if (4 * q4 < i) {
+          const f32x4 rv = *reinterpret_cast<const f32x4*>(&sR[i][4 * q4]);  // broadcast
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (4 * q4 + t < i) acc -= rv[t] * x[4 * q4 + t];
+        }
+      }
       x[i] = acc;
     }
     const float bc = sBeta[c];
 #pragma unroll
-    for (int i = 0; i < kC; ++i) sM[i][c] = x[i] * bc;  // Mb = A_kk B
+    for (int i = 0; i < kC; ++i) sM[i][c] = x[i] * bc;
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- -Mb and -(A_qk Mb) as BF16 MFMA operands; Mb / A_qk records ----------------
+  // ---- P = A_qk Mb ---------------------------------------------------------------
   {
     const int mi = tid >> 4;
     const int c = tid & 15;
-    float P = 0.f;
+    float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < kC; ++i) P += sA[mi][i] * sM[i][c];
-    sNP[mi][c] = float_to_bf16_bits(-P);
-    sNM[mi][c] = float_to_bf16_bits(-sM[mi][c]);
-    if (tid < 64) {  // [L 64][Mb j 4, A_qk j 4]
-      const int L = tid;
-      const int mm = L & 15, g2 = L >> 4;
-      unsigned short out[8];
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&sA[mi][4 * i4]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        out[j] = float_to_bf16_bits(sM[mm][4 * g2 + j]);
-        out[4 + j] = float_to_bf16_bits(sA[mm][4 * g2 + j]);
-      }
-      *reinterpret_cast<u32x4*>(rec + kOffMbAq + 16 * L) = *reinterpret_cast<const u32x4*>(out);
+      for (int t = 0; t < 4; ++t) acc += av[t] * sM[4 * i4 + t][c];
     }
+    sP[mi][c] = acc;
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- Kn = -Mb K_start^T and Qt = s Q_start^T - (A_qk Mb) K_start^T on MFMA --------
+  // ---- Kn^T = -K_start^T Mb^T and Qt^T = s Q_start^T - K_start^T P^T on MFMA --------
+  // With the key blocks as MFMA rows, lane (grp, m) of block b ends up holding
+  // Kn[m][16 b + 4 grp + j], which is the record's operand order: wave kb writes the
+  // pieces of key blocks 2 kb and 2 kb + 1 directly.
   {
-    const i16x4 aM = *reinterpret_cast<const i16x4*>(&sNM[m][4 * grp]);
-    const i16x4 aP = *reinterpret_cast<const i16x4*>(&sNP[m][4 * grp]);
+    const int kb = wave;
+    const f32x4 mrow = *reinterpret_cast<const f32x4*>(&sM[m][4 * grp]);
+    const f32x4 prow = *reinterpret_cast<const f32x4*>(&sP[m][4 * grp]);
+    const i16x4 bM = pack4(-mrow);  // B[token 4 grp + j][token m] = -Mb[m][4 grp + j]
+    const i16x4 bP = pack4(-prow);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    i16x4 kn[2], qt[2];
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int b = 2 * wave + bb;  // 16-key block
-      i16x4 bk;
+    for (int half = 0; half < 2; ++half) {
+      const int b = 2 * kb + half;
+      i16x4 a;  // A[key 16 b + m][token 4 grp + j] = K_start[4 grp + j][16 b + m]
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bk[j] = static_cast<short>(sKs[4 * grp + j][16 * b + m]);
-      f32x4 qt;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qt[j] = sQf[4 * grp + j][16 * b + m];
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 kn = mfma16(aM, bk, zero);
-      qt = mfma16(aP, bk, qt);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sG[4 * grp + j][16 * b + m] = kn[j];
-        sQf[4 * grp + j][16 * b + m] = qt[j];
-      }
+      for (int j = 0; j < 4; ++j) a[j] = static_cast<short>(sKs[4 * grp + j][16 * b + m]);
+      const f32x4 qinit = *reinterpret_cast<const f32x4*>(&sQf[m][16 * b + 4 * grp]);
+      kn[half] = pack4(mfma16(a, bM, zero));
+      qt[half] = pack4(mfma16(a, bP, qinit));
     }
-  }
-  __syncthreads();
-
-  // ---- Kn and Qt records in the recurrence's operand order --------------------------
-  {
-    const int f0 = 8 * tid;  // [kb 4][L 64][e 8]
-    const int kb = f0 >> 9;
-    const int L = (f0 >> 3) & 63;
-    const int mm = L & 15, g2 = L >> 4;
-    unsigned short a[8], b[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = 32 * kb + 16 * (e >> 2) + 4 * g2 + (e & 3);
-      a[e] = float_to_bf16_bits(sG[mm][key]);
-      b[e] = float_to_bf16_bits(sQf[mm][key]);
+    const u32x2 k0 = __builtin_bit_cast(u32x2, kn[0]), k1 = __builtin_bit_cast(u32x2, kn[1]);
+    const u32x2 q0 = __builtin_bit_cast(u32x2, qt[0]), q1 = __builtin_bit_cast(u32x2, qt[1]);
+    *reinterpret_cast<u32x4*>(rec + kOffKn + kb * 1024 + lane * 16) = u32x4{k0[0], k0[1], k1[0], k1[1]};
+    *reinterpret_cast<u32x4*>(rec + kOffQt + kb * 1024 + lane * 16) = u32x4{q0[0], q0[1], q1[0], q1[1]};
+    if (wave == 0) {  // [L 64][Mb j 4, A_qk j 4]
+      const f32x4 arow = *reinterpret_cast<const f32x4*>(&sA[m][4 * grp]);
+      const u32x2 mb = __builtin_bit_cast(u32x2, pack4(mrow));
+      const u32x2 aq = __builtin_bit_cast(u32x2, pack4(arow));
+      *reinterpret_cast<u32x4*>(rec + kOffMbAq + 16 * lane) = u32x4{mb[0], mb[1], aq[0], aq[1]};
     }
-    *reinterpret_cast<u32x4*>(rec + kOffKn + 16 * tid) = *reinterpret_cast<const u32x4*>(a);
-    *reinterpret_cast<u32x4*>(rec + kOffQt + 16 * tid) = *reinterpret_cast<const u32x4*>(b);
   }
 }
 
