@@ -349,6 +349,9 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   }
   const bool io_bf16 = a->io_dtype == KDA_BF16;
   const bool st_bf16 = a->state_dtype == KDA_BF16;
+  auto recurrence = [&](int64_t wgs) {
+    return kda::launch_recurrence(p, wgs, io_bf16, st_bf16, stream);
+  };
   hipEvent_t* ev = nullptr;
   if (a->trace_events && a->n_trace_events >= 3)
     ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(a->trace_events));
@@ -361,22 +364,20 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
   if (pl.seg_len == 0) {
     const int64_t wgs = a->N * a->H * (KDA_HEAD_DIM / rows);
-    if (e == hipSuccess) e = kda::launch_recurrence(p, wgs, io_bf16, st_bf16, stream);
+    if (e == hipSuccess) e = recurrence(wgs);
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[3], stream);
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[4], stream);
   } else {
     p.mode = kda::kModeScanA;
     p.blocks = 2 * KDA_HEAD_DIM / rows;
-    if (e == hipSuccess)
-      e = kda::launch_recurrence(p, a->H * pl.seg_stride * p.blocks, io_bf16, st_bf16, stream);
+    if (e == hipSuccess) e = recurrence(a->H * pl.seg_stride * p.blocks);
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[3], stream);
     if (e == hipSuccess && (a->cu_seqlens || pl.segs_per_seq >= 3))
       e = kda::launch_combine(p, stream);
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[4], stream);
     p.mode = kda::kModeScanC;
     p.blocks = KDA_HEAD_DIM / rows;
-    if (e == hipSuccess)
-      e = kda::launch_recurrence(p, a->H * pl.seg_stride * p.blocks, io_bf16, st_bf16, stream);
+    if (e == hipSuccess) e = recurrence(a->H * pl.seg_stride * p.blocks);
   }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s", hipGetErrorString(e));

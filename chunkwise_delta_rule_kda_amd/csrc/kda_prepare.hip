@@ -185,7 +185,6 @@ __global__ __launch_bounds__(256) void kda_prepare_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int64_t h = blockIdx.y;
-  const int64_t H = p.H;
   // Thread (r, c8): token r = tid % 16, channels 8 c8 .. 8 c8 + 7, c8 = tid / 16, so the
   // 16 tokens of a channel group form one 16-lane row (the prefix over tokens is a
   // row scan).

@@ -104,6 +104,14 @@ struct Tile {
   static_assert(kSlots * SLOT <= 65536, "LDS ring");
 };
 
+// Column of row r of Phi in its stored transpose: r = 32 kk + 16 h + 4 grp + i (the key
+// order of the MFMA operands) is stored at 32 kk + 8 grp + 4 h + i, so that the eight
+// entries one lane of the combine needs for one 16x16x32 product are contiguous.
+__device__ __forceinline__ int phi_col(int r) {
+  const int kk = r >> 5, h = (r >> 4) & 1, grp = (r >> 2) & 3, i = r & 3;
+  return 32 * kk + 8 * grp + 4 * h + i;
+}
+
 // Where one workgroup's run starts, what it reads and what it writes.
 enum StartKind : int { kStartIn = 0, kStartZero = 1, kStartIdentity = 2, kStartScan = 3 };
 
@@ -365,10 +373,8 @@ __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f
 // Unit u = lt + k * LT of a chunk is record byte 16 u (u < 864), V-tile piece u - 864
 // (token row, 16-byte part), or padding (re-reads record unit 0 into the slot's unused
 // tail). Chunks past the run's end re-read its last chunk (in bounds, never used).
-template <bool BF16IO, int W>
-__device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_u8* ring,
-                                            int lt) {
-  using T = Tile<BF16IO, W>;
+template <bool BF16IO, typename T>
+__device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_u8* ring, int lt) {
   const int64_t vstride_b = p.H * kD * T::ES;
   const unsigned char* rec0 =
       p.records + (t.h * p.max_chunks + t.rec_chunk) * static_cast<int64_t>(kRecord);
@@ -420,9 +426,10 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
   auto put = [&](const u32x4(&src)[T::K], int slot) {
     lds_u8* s = ring + slot * T::SLOT;
 #pragma unroll
-    for (int k = 0; k < T::K; ++k)
+    for (int k = 0; k < T::K; ++k) {
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(s + (lt + k * T::LT) * 16) =
           src[k];
+    }
   };
 #pragma unroll
   for (int d = 0; d < T::DEPTH; ++d) issue(r[d], d);
@@ -542,12 +549,13 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
 #pragma unroll
     for (int b = 0; b < 8; ++b) store4<false>(t.s_dst, lrow + 16 * b + 4 * grp, st[b]);
   }
-  if (t.phi_dst) {  // transposed: [key][row]
+  if (t.phi_dst) {  // transposed, [key][phi_col(row)]
+    const int col = phi_col(v0 + m);
 #pragma unroll
     for (int b = 0; b < 8; ++b)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        t.phi_dst[(16 * b + 4 * grp + j) * kD + v0 + m] = float_to_bf16_bits(st[b][j]);
+        t.phi_dst[(16 * b + 4 * grp + j) * kD + col] = float_to_bf16_bits(st[b][j]);
   }
 }
 
@@ -568,18 +576,23 @@ __global__ __launch_bounds__(block_threads(W), 2) void kda_recurrence_kernel(Par
   if (wave < W)
     compute_loop<BF16IO, BF16ST, W>(p, t, ring, wave, lane);
   else if (t.nch > 0)
-    loader_loop<BF16IO, W>(p, t, ring, static_cast<int>(threadIdx.x) - 64 * W);
+    loader_loop<BF16IO, T>(p, t, ring, static_cast<int>(threadIdx.x) - 64 * W);
 }
 
 // Launch B of the segmented form: S_{p+1} = S_p Phi_p + Z_p, p = 1 .. P-2, for 64 value
 // rows of one (sequence, head) per workgroup (4 waves x 16 rows). In the transposed
 // form S^T_{p+1} = Phi_p^T S_p^T + Z_p^T the accumulator of one step is, after BF16
 // packing, the B operand of the next (the key permutation the recurrence uses), and
-// Phi_p^T (stored [key][row] by launch A) is the A operand, staged through LDS.
+// Phi_p^T (stored [key][phi_col(row)] by launch A) is the A operand: one 16-byte LDS
+// read per product. Phi_p goes through a 3-buffer LDS ring, fetched three steps ahead
+// (its producer ran on other compute units, so every fetch comes from far memory), and
+// Z_p two steps ahead in registers.
 constexpr int kPhiRow = kD * 2 + 16;  // LDS row pitch of Phi^T (bytes), padded for banks
+constexpr int kPhiBuf = kD * kPhiRow;
+constexpr int kPhiBufs = 3;
 
 __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) unsigned char phi_[kD * kPhiRow];
+  __shared__ __attribute__((aligned(16))) unsigned char phi_[kPhiBufs * kPhiBuf];
   lds_u8* phi = (lds_u8*)(phi_);
   const int64_t task = blockIdx.x;  // (h * N + n) * 2 + half
   const int half = static_cast<int>(task & 1);
@@ -600,65 +613,82 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   const int64_t slot0 = h * p.seg_stride + first;
   float* sbase = p.scan_s + slot0 * (kD * kD);
   const unsigned short* pbase = p.scan_phi + slot0 * (kD * kD);
+  const int64_t last = nseg - 2;  // steps s = 1 .. last
 
-  f32x4 st[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) st[b] = load4<false>(sbase + 1 * (kD * kD), lrow + 16 * b + 4 * grp);
-  // Phi^T rows (keys) of 256 B: thread tid copies 16-byte pieces tid + 256 i, i < 8.
-  u32x4 pr[8];
-  auto fetch_phi = [&](int64_t s) {
+  // Phi_s^T rows (keys) of 256 B: thread tid copies 16-byte pieces tid + 256 i, i < 8.
+  auto fetch_phi = [&](u32x4 (&dst)[8], int64_t s) {
+    s = s < last ? s : last;  // past the last step: re-read it (in bounds, unused)
     const unsigned char* src = reinterpret_cast<const unsigned char*>(pbase + s * (kD * kD));
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      pr[i] = *reinterpret_cast<const u32x4*>(src + (tid + 256 * i) * 16);
+    for (int i = 0; i < 8; ++i) dst[i] = *reinterpret_cast<const u32x4*>(src + (tid + 256 * i) * 16);
   };
-  f32x4 z[8];
-  auto fetch_z = [&](int64_t s) {
-#pragma unroll
-    for (int b = 0; b < 8; ++b) z[b] = load4<false>(sbase + s * (kD * kD), lrow + 16 * b + 4 * grp);
-  };
-  fetch_phi(1);
-  fetch_z(2);
-#pragma unroll 1
-  for (int64_t s = 1; s + 1 < nseg; ++s) {
+  auto put_phi = [&](const u32x4 (&src)[8], int64_t s) {
+    lds_u8* buf = phi + (s % kPhiBufs) * kPhiBuf;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int piece = tid + 256 * i;  // 16 pieces per key row
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-          phi + (piece >> 4) * kPhiRow + (piece & 15) * 16) = pr[i];
+          buf + (piece >> 4) * kPhiRow + (piece & 15) * 16) = src[i];
     }
-    f32x4 zc[8];
+  };
+  // Z_s lives in slot s + 1 and becomes S_{s+1} there.
+  auto fetch_z = [&](f32x4 (&dst)[8], int64_t s) {
+    s = s < last ? s : last;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) zc[b] = z[b];
-    lds_barrier();
-    if (s + 2 < nseg) {  // prefetch the next step's operands
-      fetch_phi(s + 1);
-      fetch_z(s + 2);
-    }
+    for (int b = 0; b < 8; ++b) dst[b] = load4<false>(sbase + (s + 1) * (kD * kD), lrow + 16 * b + 4 * grp);
+  };
+
+  f32x4 st[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) st[b] = load4<false>(sbase + 1 * (kD * kD), lrow + 16 * b + 4 * grp);
+  u32x4 pr[8];
+  f32x4 za[8], zb[8];  // Z of the even / odd steps
+  fetch_phi(pr, 1);
+  put_phi(pr, 1);
+  fetch_phi(pr, 2);
+  put_phi(pr, 2);
+  fetch_z(za, 1);
+  fetch_z(zb, 2);
+  fetch_phi(pr, 3);
+  lds_barrier();
+  // One step: S_{s+1} = S_s Phi_s + Z_s, then the staging for later steps. Two steps per
+  // loop iteration (za, zb alternate), so that the wait counts the compiler derives at
+  // the loop head are those of the steady state.
+  auto step = [&](int64_t s, f32x4 (&z)[8]) {
+    const lds_u8* buf = phi + (s % kPhiBufs) * kPhiBuf;
     bf16x8 sp[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sp[kb] = pack8(st[2 * kb], st[2 * kb + 1]);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      // A[key 16 b + m][r] with r = 32 kk + 16 (e / 4) + 4 grp + e % 4 (the B layout).
-      const lds_u8* row = phi + (16 * b + m) * kPhiRow + 8 * grp;
+      const lds_u8* row = buf + (16 * b + m) * kPhiRow + 16 * grp;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const i16x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) i16x4*>(
-            row + kk * 64);
-        const i16x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) i16x4*>(
-            row + kk * 64 + 32);
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 a =
+            *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(row + kk * 64);
         acc = mfma32(a, sp[kk], acc);
       }
-      st[b] = acc + zc[b];
+      st[b] = acc + z[b];
     }
+    // Keep this order: the products first; then the registers fetched one step ago go
+    // to LDS (waiting only for those loads), and only then the next fetches are issued.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 8; ++b) store4<false>(sbase + (s + 1) * (kD * kD), lrow + 16 * b + 4 * grp, st[b]);
-    lds_barrier();  // every wave is done with this Phi before the next is written
+    put_phi(pr, s + 2);  // buffer of step s - 1, released at the previous barrier
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_z(z, s + 2);
+    fetch_phi(pr, s + 3);
+    lds_barrier();
+  };
+  int64_t s = 1;
+#pragma unroll 1
+  for (; s + 1 <= last; s += 2) {
+    step(s, za);
+    step(s + 1, zb);
   }
+  if (s <= last) step(s, za);
 }
 
 template <bool BF16IO, bool BF16ST>
