@@ -8,8 +8,9 @@ Default workload: T = 8192 tokens, H = 6 heads, d = 128, BF16 (one GPU's share o
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu-baseline]
                     [--extra-configs 2,3] [--calib-copy-mib 1024]
 
-Per-kernel durations come from HIP events the library records between its launches on
-the call's stream, accumulated over the timed steps.
+The step time comes from the timed calls alone. Per-kernel durations come from a second
+pass in which the library records HIP events between its launches on the call's stream;
+the stream time of one event record (measured in the same run) is subtracted from each.
 """
 
 import argparse
@@ -76,6 +77,8 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.restype = ctypes.c_int
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventRecord.restype = ctypes.c_int
 
     def create(self, n):
         out = []
@@ -86,6 +89,11 @@ class HipEvents:
                 raise RuntimeError(f"hipEventCreate failed: {rc}")
             out.append(e.value)
         return out
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -125,36 +133,58 @@ def make_call(x, device, **extra):
 
 
 def time_config(x, steps, warmup, device, hip, **extra):
+    """Three passes over `steps` calls each:
+    1. untimed-inside: the calls back to back between two events (the step time);
+    2. traced: the library records five events per call between its launches, giving
+       the prepare / first recurrence launch / combine / re-run durations;
+    3. calibration: two events recorded back to back, `steps` times. Each traced phase
+       spans exactly one event record (its start marker), whose stream time is this
+       gap; it is subtracted from every phase."""
     import torch
 
     call, _ = make_call(x, device, **extra)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    # Events per step: start, after prepare, after the last recurrence launch, after
-    # the first recurrence launch, after the segment combine (see kda.h).
-    E = 5
-    evs = hip.create(E * steps)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
-    for i in range(steps):
-        call(trace=evs[E * i:E * i + E])
+    for _ in range(steps):
+        call()
     stop.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
+
+    # Events per call: start, after prepare, after the last recurrence launch, after the
+    # first recurrence launch, after the segment combine (see kda.h).
+    E = 5
+    evs = hip.create(E * steps)
+    for i in range(steps):
+        call(trace=evs[E * i:E * i + E])
+    torch.cuda.synchronize()
     ev = lambda i, j: evs[E * i + j]
-    prep = [hip.elapsed_ms(ev(i, 0), ev(i, 1)) for i in range(steps)]
-    rec = [hip.elapsed_ms(ev(i, 1), ev(i, 2)) for i in range(steps)]
-    rec_a = [hip.elapsed_ms(ev(i, 1), ev(i, 3)) for i in range(steps)]
-    comb = [hip.elapsed_ms(ev(i, 3), ev(i, 4)) for i in range(steps)]
-    rec_c = [hip.elapsed_ms(ev(i, 4), ev(i, 2)) for i in range(steps)]
+    raw = lambda a, b: [hip.elapsed_ms(ev(i, a), ev(i, b)) for i in range(steps)]
+    prep, rec, rec_a, comb, rec_c = raw(0, 1), raw(1, 2), raw(1, 3), raw(3, 4), raw(4, 2)
     hip.destroy(evs)
-    return dict(ms_per_step=total_ms / steps, wall_s=t_wall, prep_ms=prep, rec_ms=rec,
-                rec_a_ms=rec_a, combine_ms=comb, rec_c_ms=rec_c)
+
+    cal = hip.create(2 * steps)
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(steps):
+        hip.record(cal[2 * i], stream)
+        hip.record(cal[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    gap = statistics.median(hip.elapsed_ms(cal[2 * i], cal[2 * i + 1]) for i in range(steps))
+    hip.destroy(cal)
+    fix = lambda xs: [max(0.0, v - gap) for v in xs]
+    # The serial form has no combine or re-run launch: those phases hold only markers.
+    serial = statistics.median(comb) <= 1.5 * gap and statistics.median(rec_c) <= 1.5 * gap
+    return dict(ms_per_step=total_ms / steps, wall_s=t_wall, prep_ms=fix(prep),
+                rec_ms=[max(0.0, v - 3 * gap) for v in rec],  # ev 1 -> 2 spans three records
+                rec_a_ms=fix(rec_a), combine_ms=[0.0] * steps if serial else fix(comb),
+                rec_c_ms=[0.0] * steps if serial else fix(rec_c), event_gap_ms=gap,
+                serial=serial)
 
 
 def cpu_baseline(x, budget_s=10.0, max_reps=30):
@@ -208,6 +238,7 @@ def summarize(x, r):
             first=round(statistics.mean(r["rec_a_ms"]) * 1e3, 2),
             combine=round(statistics.mean(r["combine_ms"]) * 1e3, 2),
             rerun=round(statistics.mean(r["rec_c_ms"]) * 1e3, 2)),
+        event_marker_us=round(r["event_gap_ms"] * 1e3, 2),
     )
 
 
@@ -253,17 +284,23 @@ def main():
     main_s = summarize(x, r)
     progress(f"config{args.config}: {main_s}")
 
-    # Dominant kernel: the recurrence (the serial chain). Roofline on its MFMA work.
-    rec_us = statistics.mean(r["rec_ms"]) * 1e3
+    # Dominant kernel: the recurrence kernel (the serial chain), one launch per call in the
+    # serial form, two (the first segments and the re-run) in the segmented form. Roofline
+    # on its algorithmic MFMA work (the method's contractions, split evenly over the
+    # launches) per average launch duration.
+    launches = 1 if r["serial"] else 2
+    kern_us = (statistics.mean(r["rec_a_ms"]) + statistics.mean(r["rec_c_ms"])) * 1e3
+    avg_launch_us = kern_us / launches
     th = x.tokens() * x.H
     rec_flop = th * FLOP_REC_PER_TOKEN_HEAD
-    achieved = rec_flop / (rec_us * 1e-6) / 1e12
+    achieved = rec_flop / launches / (avg_launch_us * 1e-6) / 1e12
     workload = f"config{args.config}"
     roofline = dict(bound="mfma", kernel="kda_recurrence", achieved=round(achieved, 3),
                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 6),
                     traffic=traffic_from_profiles("kda_recurrence", workload),
-                    avg_launch_us=round(rec_us, 3))
+                    avg_launch_us=round(avg_launch_us, 3), launches_per_call=launches,
+                    flop_per_launch=rec_flop / launches)
 
     per_config = {workload: main_s}
     for c in [int(c) for c in args.extra_configs.split(",") if c.strip()]:

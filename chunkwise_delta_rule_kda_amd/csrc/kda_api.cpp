@@ -172,6 +172,23 @@ Plan make_plan(const kda_prefill_args* a) {
 
 size_t workspace_need(const kda_prefill_args* a) { return make_plan(a).total; }
 
+// Workgroups of launches A and C of the segmented form. Fixed layout: the active row
+// blocks only (per sequence b0 for segment 0 and 2 b0 for each of segments 1 .. P-2 in
+// A, b0 for each of segments 1 .. P-1 in C, b0 = 128 / rows). Varlen: every scan slot
+// of the bound times the row blocks; workgroups past a sequence's segments exit.
+int64_t scan_a_workgroups(const kda_prefill_args* a, const Plan& pl, int rows) {
+  const int64_t b0 = KDA_HEAD_DIM / rows;
+  if (a->cu_seqlens) return a->H * pl.seg_stride * 2 * b0;
+  const int64_t P = pl.segs_per_seq;
+  return a->H * a->N * (P >= 2 ? b0 + 2 * b0 * (P - 2) : b0);
+}
+
+int64_t scan_c_workgroups(const kda_prefill_args* a, const Plan& pl, int rows) {
+  const int64_t b0 = KDA_HEAD_DIM / rows;
+  if (a->cu_seqlens) return a->H * pl.seg_stride * b0;
+  return a->H * a->N * (pl.segs_per_seq - 1) * b0;
+}
+
 // Rows per workgroup of the recurrence launches: the explicit choice, else 64 in the
 // segmented form (launch A alone has about one workgroup per compute unit) and the
 // fill rule in the serial form.
@@ -295,9 +312,9 @@ kda_status kda_prefill_plan(const kda_prefill_args* a, int32_t num_cus, kda_plan
   out->segment_chunks = pl.seg_len;
   out->segments_per_head_bound = pl.seg_stride;
   if (pl.seg_len > 0) {
-    out->recurrence_workgroups = a->H * pl.seg_stride * (2 * KDA_HEAD_DIM / rows);
-    out->scan_c_workgroups = a->H * pl.seg_stride * (KDA_HEAD_DIM / rows);
-    out->combine_workgroups = a->H * a->N * 2;
+    out->recurrence_workgroups = scan_a_workgroups(a, pl, rows);
+    out->scan_c_workgroups = scan_c_workgroups(a, pl, rows);
+    out->combine_workgroups = a->H * a->N * 8;
   } else {
     out->recurrence_workgroups = a->N * a->H * (KDA_HEAD_DIM / rows);
   }
@@ -370,14 +387,14 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   } else {
     p.mode = kda::kModeScanA;
     p.blocks = 2 * KDA_HEAD_DIM / rows;
-    if (e == hipSuccess) e = recurrence(a->H * pl.seg_stride * p.blocks);
+    if (e == hipSuccess) e = recurrence(scan_a_workgroups(a, pl, rows));
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[3], stream);
     if (e == hipSuccess && (a->cu_seqlens || pl.segs_per_seq >= 3))
       e = kda::launch_combine(p, stream);
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[4], stream);
     p.mode = kda::kModeScanC;
     p.blocks = KDA_HEAD_DIM / rows;
-    if (e == hipSuccess) e = recurrence(a->H * pl.seg_stride * p.blocks);
+    if (e == hipSuccess) e = recurrence(scan_c_workgroups(a, pl, rows));
   }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s", hipGetErrorString(e));

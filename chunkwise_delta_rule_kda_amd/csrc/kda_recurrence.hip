@@ -169,6 +169,9 @@ __device__ __forceinline__ void seq_segments(const Params& p, int64_t n, int64_t
   }
 }
 
+__device__ bool segment_task(const Params& p, Task& t, int64_t h, int64_t n, int64_t seg,
+                             int64_t first, int64_t nseg, int vr);
+
 __device__ bool decode_task(const Params& p, int rows, Task& t) {
   const int64_t task = task_index();
   const int64_t H = p.H;
@@ -196,6 +199,39 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
     t.start = kStartIn;
     return true;
   }
+  // Fixed layout: only the active row blocks are launched. Per sequence, launch A has
+  // the b0 = 128 / rows value blocks of segment 0, then for segments 1 .. P-2 the b0
+  // value (Z) and b0 transition (Phi) blocks; launch C the b0 value blocks of segments
+  // 1 .. P-1. Varlen: a bound of seg_stride slots x p.blocks per head, decoded below.
+  if (!p.cu_seqlens) {
+    const int b0 = kD / rows;
+    const int64_t P = p.segs_per_seq;
+    const int64_t per_seq = p.mode == kModeScanA ? (P >= 2 ? b0 + 2 * b0 * (P - 2) : b0)
+                                                 : (P - 1) * b0;
+    if (per_seq <= 0) return false;
+    const int64_t per_head = p.N * per_seq;
+    const int64_t h = task / per_head;
+    if (h >= H) return false;
+    const int64_t rem = task - h * per_head;
+    const int64_t n = rem / per_seq;
+    int64_t u = rem - n * per_seq;
+    int64_t seg;
+    int vr;
+    if (p.mode == kModeScanA) {
+      if (u < b0) {
+        seg = 0;
+      } else {
+        u -= b0;
+        seg = 1 + u / (2 * b0);
+        u -= (seg - 1) * 2 * b0;
+      }
+    } else {
+      seg = 1 + u / b0;
+      u -= (seg - 1) * b0;
+    }
+    vr = static_cast<int>(u) * rows;
+    return segment_task(p, t, h, n, seg, n * P, P, vr);
+  }
   const int blocks = p.blocks;
   const int64_t per_head = p.seg_stride * blocks;
   const int64_t h = task / per_head;
@@ -204,7 +240,7 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
   const int blk = static_cast<int>(rem - gsg * blocks);
   if (h >= H) return false;
   int64_t n;
-  if (p.cu_seqlens) {
+  {
     if (gsg >= p.cu_segs[p.N]) return false;
     int64_t lo = 0, hi = p.N - 1;  // largest n with cu_segs[n] <= gsg
     while (lo < hi) {
@@ -213,15 +249,29 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
       else hi = mid - 1;
     }
     n = lo;
-  } else {
-    n = gsg / p.segs_per_seq;
-    if (n >= p.N) return false;
   }
-  int64_t first, nseg, start, end, chunk0, nch;
+  int64_t first, nseg;
   seq_segments(p, n, first, nseg);
-  seq_range(p, n, start, end, chunk0, nch);
   const int64_t seg = gsg - first;
-  if (seg < 0 || seg >= nseg || first + nseg > p.seg_stride) return false;
+  const int vr = blk * rows;
+  if (p.mode == kModeScanA) {
+    if (nseg >= 2 && seg == nseg - 1) return false;  // last segment: only in launch C
+    if (vr >= kD && seg == 0) return false;           // no transition for segment 0
+  } else if (seg == 0) {
+    return false;                                     // segment 0: only in launch A
+  }
+  return segment_task(p, t, h, n, seg, first, nseg, vr);
+}
+
+// Task of row block vr (0 .. 255 in launch A: value rows, then the rows of Phi) of
+// segment seg of sequence n (global segments first .. first + nseg - 1) of head h.
+__device__ bool segment_task(const Params& p, Task& t, int64_t h, int64_t n, int64_t seg,
+                             int64_t first, int64_t nseg, int vr) {
+  if (seg < 0 || seg >= nseg || first < 0 || first + nseg > p.seg_stride) return false;
+  const int64_t gsg = first + seg;
+  int64_t start, end, chunk0, nch;
+  seq_range(p, n, start, end, chunk0, nch);
+  const int64_t H = p.H;
   const int64_t c0 = seg * p.seg_len;
   const int64_t c1 = min(c0 + p.seg_len, nch);
   t.tok0 = start + c0 * kC;
@@ -231,9 +281,7 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
   t.sh = n * H + h;
   t.h = h;
   const int64_t slot = h * p.seg_stride + gsg;  // scan slot of this segment
-  const int vr = blk * rows;
   if (p.mode == kModeScanA) {
-    if (nseg >= 2 && seg == nseg - 1) return false;  // last segment: only in launch C
     if (vr < kD) {
       t.vwg = vr;
       t.start = seg == 0 ? kStartIn : kStartZero;
@@ -241,7 +289,6 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
       t.final_state = nseg == 1;
       if (nseg >= 2) t.s_dst = p.scan_s + (slot + 1) * (kD * kD);  // S_1, or Z_seg
     } else {
-      if (seg == 0) return false;
       t.vwg = vr - kD;
       t.start = kStartIdentity;
       t.vzero = true;
@@ -252,7 +299,6 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
     return true;
   }
   // launch C
-  if (seg == 0) return false;
   t.vwg = vr;
   t.start = kStartScan;
   t.s_src = p.scan_s + slot * (kD * kD);
@@ -301,6 +347,8 @@ __device__ __forceinline__ void read_chain(ChainIn& x, const lds_u8* slot, int l
   }
 }
 
+// OUT: the operands of the output (Qt) are read only by runs that write O.
+template <bool OUT>
 __device__ __forceinline__ void read_tail(TailIn& x, const lds_u8* slot, int lane) {
 #pragma unroll
   for (int bp = 0; bp < 4; ++bp)
@@ -308,9 +356,13 @@ __device__ __forceinline__ void read_tail(TailIn& x, const lds_u8* slot, int lan
         slot + kOffKeT + bp * 1024 + lane * 16);
   x.dv = *reinterpret_cast<const __attribute__((address_space(3))) f32x2*>(slot + kOffD + lane * 8);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    x.qt[kb] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-        slot + kOffQt + kb * 1024 + lane * 16);
+  for (int kb = 0; kb < 4; ++kb) {
+    if constexpr (OUT)
+      x.qt[kb] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+          slot + kOffQt + kb * 1024 + lane * 16);
+    else
+      x.qt[kb] = bf16x8{};
+  }
 }
 
 // Lane N of this lane's 16-lane row (DPP row broadcast).
@@ -343,7 +395,9 @@ __device__ __forceinline__ void state_update(f32x4 (&st)[8], const TailIn& b, i1
   }
 }
 
-// One chunk for one wave: updates the state and returns O[value 4 grp + j][token m].
+// One chunk for one wave: updates the state and returns O[value 4 grp + j][token m]
+// (zero when OUT is false: runs that write no O skip its products).
+template <bool OUT>
 __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f32x4 (&st)[8],
                                             bf16x8 (&sp)[4]) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -360,6 +414,7 @@ __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f
   state_update<0>(st, b, up);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) sp[kb] = pack8(st[2 * kb], st[2 * kb + 1]);
+  if constexpr (!OUT) return zero;
   // O from the entering state (off the chain)
   f32x4 out = mfma32(s0, b.qt[0], zero);
   out = mfma32(s1, b.qt[1], out);
@@ -373,8 +428,13 @@ __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f
 // Unit u = lt + k * LT of a chunk is record byte 16 u (u < 864), V-tile piece u - 864
 // (token row, 16-byte part), or padding (re-reads record unit 0 into the slot's unused
 // tail). Chunks past the run's end re-read its last chunk (in bounds, never used).
-template <bool BF16IO, typename T>
+// OUT false: the record units that hold Qt (whole iterations k of the unit loop, for both
+// loader widths) are neither loaded nor written.
+template <bool BF16IO, typename T, bool OUT>
 __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_u8* ring, int lt) {
+  auto skipped = [](int k) {
+    return !OUT && k * T::LT >= kOffQt / 16 && (k + 1) * T::LT <= (kOffQt + 4096) / 16;
+  };
   const int64_t vstride_b = p.H * kD * T::ES;
   const unsigned char* rec0 =
       p.records + (t.h * p.max_chunks + t.rec_chunk) * static_cast<int64_t>(kRecord);
@@ -413,10 +473,12 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
     if (nvalid >= kC) {
 #pragma unroll
       for (int k = 0; k < T::K; ++k)
-        dst[k] = *reinterpret_cast<const u32x4*>(base[k] + static_cast<uint64_t>(j) * inc[k]);
+        if (!skipped(k))
+          dst[k] = *reinterpret_cast<const u32x4*>(base[k] + static_cast<uint64_t>(j) * inc[k]);
     } else {
 #pragma unroll
       for (int k = 0; k < T::K; ++k) {
+        if (skipped(k)) continue;
         const unsigned char* src = base[k] + static_cast<uint64_t>(j) * inc[k];
         if (vtok[k] >= nvalid) src -= vdrop[k];
         dst[k] = *reinterpret_cast<const u32x4*>(src);
@@ -427,6 +489,7 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
     lds_u8* s = ring + slot * T::SLOT;
 #pragma unroll
     for (int k = 0; k < T::K; ++k) {
+      if (skipped(k)) continue;
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(s + (lt + k * T::LT) * 16) =
           src[k];
     }
@@ -463,7 +526,7 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
     if (rest > 2) step(IntC<3>{}, c0 + 2);
 }
 
-template <bool BF16IO, bool BF16ST, int W>
+template <bool BF16IO, bool BF16ST, int W, bool OUT>
 __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds_u8* ring,
                                              int wave, int lane) {
   using T = Tile<BF16IO, W>;
@@ -512,7 +575,7 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
         store4<BF16IO>(p.o, obase + (c * kC + m) * vstride + 4 * grp, val);
     };
     TailIn tail;
-    read_tail(tail, ring, lane);
+    read_tail<OUT>(tail, ring, lane);
 #pragma unroll 1
     for (int64_t c = 0; c < nch; ++c) {
       const int ns = cs + 1 == kSlots ? 0 : cs + 1;  // slot of chunk c + 1
@@ -523,22 +586,23 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
       ChainIn nxt;
       TailIn ntail;
       read_chain<BF16IO, W>(nxt, ring + ns * T::SLOT, lane, wave, nvalid_of(c + 1));
-      read_tail(ntail, ring + ns * T::SLOT, lane);
+      read_tail<OUT>(ntail, ring + ns * T::SLOT, lane);
       const f32x4 prev = pend;
-      pend = chunk_step(cur, tail, st, sp);
-      if (t.out && c > 0) store_out(c - 1, prev);
+      pend = chunk_step<OUT>(cur, tail, st, sp);
+      if (OUT && c > 0) store_out(c - 1, prev);
       // Keep the reads in this iteration: without these uses the compiler sinks them to
       // the top of the next iteration, right before the MFMA chain that needs them.
       asm volatile("" ::"v"(nxt.kn[0]), "v"(nxt.kn[1]), "v"(nxt.kn[2]), "v"(nxt.kn[3]),
                    "v"(nxt.mb), "v"(nxt.aq), "v"(nxt.vv));
       asm volatile("" ::"v"(ntail.ke[0]), "v"(ntail.ke[1]), "v"(ntail.ke[2]), "v"(ntail.ke[3]),
-                   "v"(ntail.dv), "v"(ntail.qt[0]), "v"(ntail.qt[1]), "v"(ntail.qt[2]),
-                   "v"(ntail.qt[3]));
+                   "v"(ntail.dv));
+      if constexpr (OUT)
+        asm volatile("" ::"v"(ntail.qt[0]), "v"(ntail.qt[1]), "v"(ntail.qt[2]), "v"(ntail.qt[3]));
       cur = nxt;
       tail = ntail;
       cs = ns;
     }
-    if (t.out) store_out(nch - 1, pend);
+    if (OUT) store_out(nch - 1, pend);
   }
 
   if (t.final_state && p.state_out) {
@@ -573,122 +637,124 @@ __global__ __launch_bounds__(block_threads(W), 2) void kda_recurrence_kernel(Par
   // The wave index as a scalar, so that the role branch below is uniform per wave.
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & 63;
-  if (wave < W)
-    compute_loop<BF16IO, BF16ST, W>(p, t, ring, wave, lane);
-  else if (t.nch > 0)
-    loader_loop<BF16IO, T>(p, t, ring, static_cast<int>(threadIdx.x) - 64 * W);
+  const int lt = static_cast<int>(threadIdx.x) - 64 * W;
+  if (t.out) {
+    if (wave < W) compute_loop<BF16IO, BF16ST, W, true>(p, t, ring, wave, lane);
+    else if (t.nch > 0) loader_loop<BF16IO, T, true>(p, t, ring, lt);
+  } else {
+    if (wave < W) compute_loop<BF16IO, BF16ST, W, false>(p, t, ring, wave, lane);
+    else if (t.nch > 0) loader_loop<BF16IO, T, false>(p, t, ring, lt);
+  }
 }
 
-// Launch B of the segmented form: S_{p+1} = S_p Phi_p + Z_p, p = 1 .. P-2, for 64 value
-// rows of one (sequence, head) per workgroup (4 waves x 16 rows). In the transposed
-// form S^T_{p+1} = Phi_p^T S_p^T + Z_p^T the accumulator of one step is, after BF16
-// packing, the B operand of the next (the key permutation the recurrence uses), and
-// Phi_p^T (stored [key][phi_col(row)] by launch A) is the A operand: one 16-byte LDS
-// read per product. Phi_p goes through a 3-buffer LDS ring, fetched three steps ahead
-// (its producer ran on other compute units, so every fetch comes from far memory), and
-// Z_p two steps ahead in registers.
-constexpr int kPhiRow = kD * 2 + 16;  // LDS row pitch of Phi^T (bytes), padded for banks
-constexpr int kPhiBuf = kD * kPhiRow;
-constexpr int kPhiBufs = 3;
+// Launch B of the segmented form: S_{p+1} = S_p Phi_p + Z_p, p = 1 .. P-2, for 16 value
+// rows of one (sequence, head) per workgroup. In the transposed form S^T_{p+1} =
+// Phi_p^T S_p^T + Z_p^T; wave w computes output key blocks 2 w and 2 w + 1 (eight
+// 16x16x32 products). Phi_p^T, stored [key][phi_col(row)] by launch A, is the A operand:
+// each lane's eight operands of one product are one 16-byte global load, and a wave's
+// slice of Phi (32 keys x 128) is read by that wave alone, so it goes straight to
+// registers, three steps ahead together with Z. The new state, packed to BF16, is the B
+// operand of the next step; the waves exchange their packed blocks through LDS.
+// Per step a workgroup moves 32 KB of Phi, 8 KB of Z and 8 KB of S: the per-CU stream
+// rate, not the products, sets the step time, hence 16 rows (8 workgroups) per pair.
+constexpr int kCombineRows = 16;
+constexpr int kCombineDepth = 3;  // steps of Phi and Z in flight per wave
+
+struct CombineIn {
+  u32x4 a[2][4];  // Phi^T operands: output block 2 w + i, input key group kk
+  f32x4 z[2];     // Z rows v0 + m, keys 16 (2 w + i) + 4 grp + j
+};
 
 __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) unsigned char phi_[kPhiBufs * kPhiBuf];
-  lds_u8* phi = (lds_u8*)(phi_);
-  const int64_t task = blockIdx.x;  // (h * N + n) * 2 + half
-  const int half = static_cast<int>(task & 1);
-  const int64_t hn = task >> 1;
+  __shared__ __attribute__((aligned(16))) unsigned char xch_[2 * 4 * 64 * 16];
+  lds_u8* xbase = (lds_u8*)(xch_);  // address-space cast
+  const int64_t task = blockIdx.x;  // (h * N + n) * 8 + row block
+  const int rb = static_cast<int>(task & 7);
+  const int64_t hn = task >> 3;
   const int64_t h = hn / p.N;
   const int64_t n = hn - h * p.N;
   if (h >= p.H) return;
   int64_t first, nseg;
   seq_segments(p, n, first, nseg);
   if (nseg < 3 || first < 0 || first + nseg > p.seg_stride) return;  // nothing to combine
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = static_cast<int>(threadIdx.x) & 63;
   const int m = lane & 15;
   const int grp = lane >> 4;
-  const int v0 = half * 64 + 16 * wave;
-  const int64_t lrow = (v0 + m) * kD;
+  const int64_t lrow = (kCombineRows * rb + m) * kD;
   const int64_t slot0 = h * p.seg_stride + first;
   float* sbase = p.scan_s + slot0 * (kD * kD);
-  const unsigned short* pbase = p.scan_phi + slot0 * (kD * kD);
+  const unsigned char* pbase = reinterpret_cast<const unsigned char*>(p.scan_phi + slot0 * (kD * kD));
   const int64_t last = nseg - 2;  // steps s = 1 .. last
+  // This lane's operand offsets: Phi^T row 16 b + m, bytes 64 kk + 16 grp; Z / S keys
+  // 16 b + 4 grp (b = 2 wave + i).
+  const int koff0 = 16 * (2 * wave) + 4 * grp;
+  const int koff1 = koff0 + 16;
+  const int aoff = (16 * (2 * wave) + m) * (kD * 2) + 16 * grp;
 
-  // Phi_s^T rows (keys) of 256 B: thread tid copies 16-byte pieces tid + 256 i, i < 8.
-  auto fetch_phi = [&](u32x4 (&dst)[8], int64_t s) {
+  auto fetch = [&](CombineIn& x, int64_t s) {
     s = s < last ? s : last;  // past the last step: re-read it (in bounds, unused)
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(pbase + s * (kD * kD));
+    const unsigned char* ph = pbase + s * (kD * kD * 2) + aoff;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = *reinterpret_cast<const u32x4*>(src + (tid + 256 * i) * 16);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        x.a[i][kk] = *reinterpret_cast<const u32x4*>(ph + i * 16 * (kD * 2) + 64 * kk);
+    const float* z = sbase + (s + 1) * (kD * kD) + lrow;  // Z_s lives in slot s + 1
+    x.z[0] = load4<false>(z, koff0);
+    x.z[1] = load4<false>(z, koff1);
   };
-  auto put_phi = [&](const u32x4 (&src)[8], int64_t s) {
-    lds_u8* buf = phi + (s % kPhiBufs) * kPhiBuf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int piece = tid + 256 * i;  // 16 pieces per key row
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-          buf + (piece >> 4) * kPhiRow + (piece & 15) * 16) = src[i];
-    }
-  };
-  // Z_s lives in slot s + 1 and becomes S_{s+1} there.
-  auto fetch_z = [&](f32x4 (&dst)[8], int64_t s) {
-    s = s < last ? s : last;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) dst[b] = load4<false>(sbase + (s + 1) * (kD * kD), lrow + 16 * b + 4 * grp);
+  // [parity 2][wave 4][lane 64] packed S^T blocks 2 w, 2 w + 1
+  auto xch = [&](int parity, int w) {
+    return reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
+        xbase + (parity * 4 + w) * 1024 + lane * 16);
   };
 
-  f32x4 st[8];
+  f32x4 st[2];
+  {
+    const float* s1 = sbase + 1 * (kD * kD) + lrow;
+    st[0] = load4<false>(s1, koff0);
+    st[1] = load4<false>(s1, koff1);
+  }
+  CombineIn in[kCombineDepth];
 #pragma unroll
-  for (int b = 0; b < 8; ++b) st[b] = load4<false>(sbase + 1 * (kD * kD), lrow + 16 * b + 4 * grp);
-  u32x4 pr[8];
-  f32x4 za[8], zb[8];  // Z of the even / odd steps
-  fetch_phi(pr, 1);
-  put_phi(pr, 1);
-  fetch_phi(pr, 2);
-  put_phi(pr, 2);
-  fetch_z(za, 1);
-  fetch_z(zb, 2);
-  fetch_phi(pr, 3);
+  for (int d = 0; d < kCombineDepth; ++d) fetch(in[d], 1 + d);
+  *xch(1, wave) = pack8(st[0], st[1]);  // S_1, read by step 1
   lds_barrier();
-  // One step: S_{s+1} = S_s Phi_s + Z_s, then the staging for later steps. Two steps per
-  // loop iteration (za, zb alternate), so that the wait counts the compiler derives at
-  // the loop head are those of the steady state.
-  auto step = [&](int64_t s, f32x4 (&z)[8]) {
-    const lds_u8* buf = phi + (s % kPhiBufs) * kPhiBuf;
+
+  // Step s: S_{s+1} = S_s Phi_s + Z_s with operands in set (s - 1) % 3; the set is then
+  // refilled with step s + 3. Whole groups of three steps are unrolled without
+  // conditions so that the compiler's wait before each step is for its own set only.
+  auto step = [&](auto set_c, int64_t s) {
+    constexpr int set = decltype(set_c)::value;
     bf16x8 sp[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sp[kb] = pack8(st[2 * kb], st[2 * kb + 1]);
+    for (int kk = 0; kk < 4; ++kk) sp[kk] = *xch(s & 1, kk);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const lds_u8* row = buf + (16 * b + m) * kPhiRow + 16 * grp;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 2; ++i) {
+      f32x4 acc = zero;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a =
-            *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(row + kk * 64);
-        acc = mfma32(a, sp[kk], acc);
-      }
-      st[b] = acc + z[b];
+      for (int kk = 0; kk < 4; ++kk)
+        acc = mfma32(__builtin_bit_cast(bf16x8, in[set].a[i][kk]), sp[kk], acc);
+      st[i] = acc + in[set].z[i];
     }
-    // Keep this order: the products first; then the registers fetched one step ago go
-    // to LDS (waiting only for those loads), and only then the next fetches are issued.
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) store4<false>(sbase + (s + 1) * (kD * kD), lrow + 16 * b + 4 * grp, st[b]);
-    put_phi(pr, s + 2);  // buffer of step s - 1, released at the previous barrier
-    __builtin_amdgcn_sched_barrier(0);
-    fetch_z(z, s + 2);
-    fetch_phi(pr, s + 3);
+    *xch((s + 1) & 1, wave) = pack8(st[0], st[1]);
+    float* out = sbase + (s + 1) * (kD * kD) + lrow;  // S_{s+1} replaces Z_s
+    store4<false>(out, koff0, st[0]);
+    store4<false>(out, koff1, st[1]);
+    fetch(in[set], s + kCombineDepth);
     lds_barrier();
   };
   int64_t s = 1;
 #pragma unroll 1
-  for (; s + 1 <= last; s += 2) {
-    step(s, za);
-    step(s + 1, zb);
+  for (; s + 2 <= last; s += 3) {
+    step(IntC<0>{}, s);
+    step(IntC<1>{}, s + 1);
+    step(IntC<2>{}, s + 2);
   }
-  if (s <= last) step(s, za);
+  if (s <= last) step(IntC<0>{}, s);
+  if (s + 1 <= last) step(IntC<1>{}, s + 1);
 }
 
 template <bool BF16IO, bool BF16ST>
@@ -730,7 +796,7 @@ hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16, 
 }
 
 hipError_t launch_combine(const Params& p, hipStream_t stream) {
-  const int64_t wgs = p.H * p.N * 2;
+  const int64_t wgs = p.H * p.N * (kD / kCombineRows);
   if (wgs <= 0) return hipSuccess;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kda_combine_kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream,

@@ -159,9 +159,11 @@ def test_plan_segments_small_head_counts():
     p = kda.kda_prefill_plan(fake(H=6, T=8192), 256)
     assert p["segment_chunks"] == 43 and p["segments_per_head_bound"] == 12
     assert p["rows_per_workgroup"] == 64
-    assert p["recurrence_workgroups"] == 6 * 12 * 4     # 256-row space: Z and Phi rows
-    assert p["scan_c_workgroups"] == 6 * 12 * 2
-    assert p["combine_workgroups"] == 6 * 2
+    # Active row blocks of 64 rows only: segment 0's value rows, then value (Z) and
+    # transition (Phi) rows of segments 1 .. 10; launch C re-runs segments 1 .. 11.
+    assert p["recurrence_workgroups"] == 6 * (2 + 4 * 10)
+    assert p["scan_c_workgroups"] == 6 * 11 * 2
+    assert p["combine_workgroups"] == 6 * 8
     records = 512 * 6 * kda.KDA_WS_RECORD
     assert p["scan_state_offset"] == records            # already 256-byte aligned
     slots = 6 * 12
@@ -179,6 +181,8 @@ def test_plan_segments_small_head_counts():
     v = kda.kda_prefill_plan(fake(H=2, T=4000, N=3, varlen=True, segment_chunks=20), 256)
     mc = (4000 + 15 * 3) // 16
     assert v["segments_per_head_bound"] == (mc + 19) // 20 + 3
+    bound = v["segments_per_head_bound"]
+    assert v["recurrence_workgroups"] == 2 * bound * 4 and v["scan_c_workgroups"] == 2 * bound * 2
     assert v["workspace_header_bytes"] == 256
     assert status(fake(segment_chunks=1 << 25)) == 10
 
