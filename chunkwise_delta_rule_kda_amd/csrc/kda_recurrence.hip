@@ -134,10 +134,12 @@ struct Task {
 
 __device__ __forceinline__ int64_t task_index() {
   // XCD-aware order: workgroup b runs on XCD b % 8; consecutive tasks (the row blocks of
-  // one run, which read the same records) go to the same XCD's L2.
+  // one run, which read the same records) go to the same XCD's L2. The grid is a
+  // multiple of 8 (launch_recurrence pads it); tasks past the real count decode to no
+  // work.
   const int64_t total = gridDim.x;
   const int64_t bid = blockIdx.x;
-  return (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
+  return (bid % 8) * (total / 8) + bid / 8;
 }
 
 // Token and chunk range of sequence n (the varlen plan's prefix, or the fixed layout).
@@ -783,6 +785,7 @@ hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16, 
                              hipStream_t stream) {
   if (workgroups <= 0) return hipSuccess;
   if (p.waves != 1 && p.waves != 2 && p.waves != 4) return hipErrorInvalidValue;
+  workgroups = (workgroups + 7) / 8 * 8;  // whole XCD rounds (see task_index)
   if (workgroups > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(workgroups));
   if (io_bf16) {

@@ -213,7 +213,10 @@ kda_status kda_debug_check_cu_seqlens(const int64_t *cu_seqlens, int64_t N, int6
 typedef struct kda_plan_info {
   int32_t rows_per_workgroup;
   int32_t waves_per_workgroup;     /* compute + loader waves of a recurrence workgroup */
-  int64_t recurrence_workgroups;   /* serial launch, or the first segmented launch */
+  int64_t recurrence_workgroups;   /* serial launch, or the first segmented launch; the
+                                      recurrence launches round their grids up to a
+                                      multiple of 8 (one round over the XCDs), and the
+                                      extra workgroups exit at once */
   int64_t prepare_workgroups;
   int64_t max_chunks;
   size_t workspace_header_bytes;
