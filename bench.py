@@ -177,6 +177,26 @@ def time_config(x, steps, warmup, device, hip, **extra):
     torch.cuda.synchronize()
     gap = statistics.median(hip.elapsed_ms(cal[2 * i], cal[2 * i + 1]) for i in range(steps))
     hip.destroy(cal)
+
+    # Per-call distribution, warm caches and with a 512 MB write between calls (evicts L2
+    # and the 256 MB MALL; untimed): each call between two events, one marker subtracted.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+    per_call = {}
+    for mode in ("warm", "flushed"):
+        ev = hip.create(2 * steps)
+        for i in range(steps):
+            if mode == "flushed":
+                flush.fill_(i & 0xFF)
+            hip.record(ev[2 * i], stream)
+            call()
+            hip.record(ev[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        us = sorted(max(0.0, hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) - gap) * 1e3
+                    for i in range(steps))
+        hip.destroy(ev)
+        per_call[mode] = dict(median=round(statistics.median(us), 2), min=round(us[0], 2),
+                              p90=round(us[min(steps - 1, int(0.9 * steps))], 2))
+    del flush
     fix = lambda xs: [max(0.0, v - gap) for v in xs]
     # The serial form has no combine or re-run launch: those phases hold only markers.
     serial = statistics.median(comb) <= 1.5 * gap and statistics.median(rec_c) <= 1.5 * gap
@@ -184,7 +204,7 @@ def time_config(x, steps, warmup, device, hip, **extra):
                 rec_ms=[max(0.0, v - 3 * gap) for v in rec],  # ev 1 -> 2 spans three records
                 rec_a_ms=fix(rec_a), combine_ms=[0.0] * steps if serial else fix(comb),
                 rec_c_ms=[0.0] * steps if serial else fix(rec_c), event_gap_ms=gap,
-                serial=serial)
+                serial=serial, per_call_us=per_call)
 
 
 def cpu_baseline(x, budget_s=10.0, max_reps=30):
@@ -239,6 +259,7 @@ def summarize(x, r):
             combine=round(statistics.mean(r["combine_ms"]) * 1e3, 2),
             rerun=round(statistics.mean(r["rec_c_ms"]) * 1e3, 2)),
         event_marker_us=round(r["event_gap_ms"] * 1e3, 2),
+        per_call_us=r["per_call_us"],
     )
 
 
@@ -278,6 +299,21 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+
+    # Achievable HBM bandwidth on this machine: a plain 1 GiB device copy (read + write).
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=device).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(5):
+        b.copy_(a)
+    s1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (s0.elapsed_time(s1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
 
     x = kda_synth.config(args.config)
     r = time_config(x, args.steps, args.warmup, device, hip)
@@ -337,6 +373,7 @@ def main():
                                f"bf16 q,k,v,g,beta; bf16 state", "global_batch": x.B,
                    "seq_len": x.T, "heads": x.H, "parallelism": "single-gpu"},
         "roofline": roofline,
+        "hbm_copy_measured_gbs": round(copy_gbs, 1),
         "cpu_baseline": cpu,
         "per_config": per_config,
         "kernel_source_hash": kernel_hash(),

@@ -15,8 +15,8 @@ Sources (cited by page title and section; no source code of any page is copied):
   "How the per-channel decay factor exp(G) enters tile computation" (split-exponent
   form), "Matrix inversion in FlashKDA" (Neumann repeated-squaring inverse) and
   "Numerical experiments on H200" (stress families).
-* "flashinfer.kda_prefill" API page: flags, varlen ``cu_seqlens`` contract and the
-  ``[N, H, V, K]`` state layout.
+* "flashinfer.kda_prefill" API page: flags, varlen ``cu_seqlens`` contract, the
+  ``[N, H, V, K]`` state layout and the state-checkpoint contract.
 
 Modules
 -------
@@ -27,7 +27,7 @@ Modules
                 the pages for ``safe_gate`` (only its range and special case are pinned).
 """
 
-from .kda_token import kda_recurrence_fp64, token_step
+from .kda_token import checkpoint_starts, kda_recurrence_fp64, token_step
 from .kda_chunk import (
     chunk_quantities,
     chunkwise_forward,
@@ -39,6 +39,7 @@ from .transforms import l2_normalize, sigmoid, safe_gate
 
 __all__ = [
     "kda_recurrence_fp64",
+    "checkpoint_starts",
     "token_step",
     "chunk_quantities",
     "chunkwise_forward",

@@ -51,6 +51,7 @@ def kda_recurrence_fp64(
     dt_bias=None,
     lower_bound=None,
     heads=None,
+    checkpoint_every=None,
 ):
     """Run the recurrence over every sequence and head, in float64.
 
@@ -63,8 +64,15 @@ def kda_recurrence_fp64(
     (token, head); beta_is_logit applies the logistic to beta; A_log / dt_bias /
     lower_bound (all given) turn g into the lower-bounded gate of ``safe_gate``.
     heads: optional list of head indices; only those heads are computed and returned.
+    checkpoint_every: optional interval I (tokens). Following the checkpoint contract of
+    the "flashinfer.kda_prefill" page (section "State and graph semantics"), every
+    non-empty sequence then contributes the states before each interval: its initial
+    state, then the states after I, 2I, ... tokens that come strictly before its end,
+    i.e. ceil(len / I) rows, stacked in sequence order (``checkpoint_starts`` gives the
+    row offsets).
 
-    Returns (o [B, T, H', V] float64, state [N, H', V, K] float64).
+    Returns (o [B, T, H', V] float64, state [N, H', V, K] float64), and with
+    checkpoint_every also checkpoints [C, H', V, K] float64.
     """
     q, k, v, g, beta = (_as64(x) for x in (q, k, v, g, beta))
     B, T, H, K = k.shape
@@ -97,12 +105,15 @@ def kda_recurrence_fp64(
 
     o = np.zeros((B * T, Hs, V), dtype=np.float64)
     states = np.zeros((N, Hs, V, K), dtype=np.float64)
+    ckpts = []
     for n, (start, end) in enumerate(bounds):
         if state0 is None:
             S = np.zeros((Hs, V, K), dtype=np.float64)
         else:
             S = np.array(_as64(state0)[n][hs], dtype=np.float64)
         for t in range(start, end):
+            if checkpoint_every is not None and (t - start) % checkpoint_every == 0:
+                ckpts.append(S.copy())  # the state before this interval
             # token_step for all heads at once: S Diag(alpha), delta-rule write, read.
             S = S * np.exp(g[t])[:, None, :]
             pred = np.matmul(S, k[t][:, :, None])[:, :, 0]
@@ -110,4 +121,14 @@ def kda_recurrence_fp64(
             S = S + u[:, :, None] * k[t][:, None, :]
             o[t] = scale * np.matmul(S, q[t][:, :, None])[:, :, 0]
         states[n] = S
+    if checkpoint_every is not None:
+        C = np.stack(ckpts) if ckpts else np.zeros((0, Hs, V, K), dtype=np.float64)
+        return o.reshape(B, T, Hs, V), states, C
     return o.reshape(B, T, Hs, V), states
+
+
+def checkpoint_starts(lengths, interval):
+    """Row offsets [N + 1] of each sequence's checkpoints: ceil(len / interval) rows per
+    sequence (none for an empty one), as on the "flashinfer.kda_prefill" page."""
+    counts = [(int(n) + interval - 1) // interval for n in lengths]
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 from oracle import (
+    checkpoint_starts,
     chunk_quantities,
     chunkwise_forward,
     inverse_explicit,
@@ -262,6 +263,48 @@ def test_split_prefill_equals_one_call():
                                  beta[:, 13:], Sa, scale=1.0)
     assert rel_err(np.concatenate([oa, ob], 1), o) < 1e-13
     assert rel_err(Sb, S) < 1e-13
+
+
+@pytest.mark.parametrize("interval", [16, 32, 7])
+def test_checkpoints_are_states_before_each_interval(interval):
+    # The flashinfer page's checkpoint contract ("State and graph semantics"): each
+    # non-empty sequence contributes its initial state, then the states after 1, 2, ...
+    # intervals that come strictly before its end: ceil(len / I) rows.
+    rng = np.random.default_rng(20)
+    lens = [0, 5, 16, 17, 40]
+    T = sum(lens)
+    q, k, v, g, beta, _ = rand_inputs(rng, 1, T, 2, 8, state=False)
+    S0 = rng.standard_normal((len(lens), 2, 8, 8))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    o, S, C = kda_recurrence_fp64(q, k, v, g, beta, S0, cu_seqlens=cu, scale=1.0,
+                                  checkpoint_every=interval)
+    o2, S2 = kda_recurrence_fp64(q, k, v, g, beta, S0, cu_seqlens=cu, scale=1.0)
+    assert np.array_equal(o, o2) and np.array_equal(S, S2)
+    starts = checkpoint_starts(lens, interval)
+    assert C.shape[0] == starts[-1] == sum(-(-n // interval) for n in lens)
+    for n, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        rows = C[starts[n]:starts[n + 1]]
+        assert len(rows) == -(-(b - a) // interval)
+        for r, row in enumerate(rows):
+            if r == 0:
+                assert np.array_equal(row, S0[n])
+                continue
+            e = a + r * interval  # state after the first r intervals of the sequence
+            _, Sr = kda_recurrence_fp64(q[:, a:e], k[:, a:e], v[:, a:e], g[:, a:e],
+                                        beta[:, a:e], S0[n:n + 1], scale=1.0)
+            assert np.array_equal(row, Sr[0])
+
+
+def test_checkpoints_closed_form_without_writes():
+    # beta = 0: checkpoint r is S0 decayed by the first r intervals' total decay.
+    rng = np.random.default_rng(21)
+    q, k, v, g, _, S0 = rand_inputs(rng, 1, 50, 2, 8)
+    beta = np.zeros((1, 50, 2))
+    _, _, C = kda_recurrence_fp64(q, k, v, g, beta, S0, scale=1.0, checkpoint_every=16)
+    assert C.shape[0] == 4
+    for r in range(4):
+        decay = np.exp(g[0, :16 * r].sum(axis=0))  # [H, K]
+        assert rel_err(C[r], S0[0] * decay[:, None, :]) < 1e-13
 
 
 # ---------------------------------------------------------------------------------
