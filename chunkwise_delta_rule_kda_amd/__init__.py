@@ -93,6 +93,10 @@ class kda_prefill_args(ctypes.Structure):
         ("flags", ctypes.c_uint32),
         ("rows_per_workgroup", ctypes.c_int32),
         ("segment_chunks", ctypes.c_int32),
+        ("checkpoint_every", ctypes.c_int64),
+        ("checkpoint_rows", ctypes.c_int64),
+        ("state_checkpoints", ctypes.c_void_p),
+        ("checkpoint_cu_starts", ctypes.c_void_p),
         ("trace_events", ctypes.c_void_p),
         ("n_trace_events", ctypes.c_int32),
     ]
@@ -113,6 +117,9 @@ class kda_plan_info(ctypes.Structure):
         ("scan_state_offset", ctypes.c_size_t),
         ("scan_transition_offset", ctypes.c_size_t),
     ]
+
+
+ABI_VERSION = 3  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
 
 
 def lib_path():
@@ -151,6 +158,9 @@ def load_library():
     lib.kda_debug_check_cu_seqlens.restype = ctypes.c_int
     lib.kda_abi_version.argtypes = []
     lib.kda_abi_version.restype = ctypes.c_int32
+    if lib.kda_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {lib.kda_abi_version()}, this binding "
+                          f"expects {ABI_VERSION}: rebuild the library")
     _LIB = lib
     return lib
 
@@ -190,7 +200,9 @@ def make_args(*, q=None, k=None, v=None, g=None, beta=None, state_in=None, cu_se
               A_log=None, dt_bias=None, o=None, state_out=None, workspace=None,
               workspace_bytes=0, B, T, H, N, D=HEAD_DIM, io_dtype=KDA_BF16,
               state_dtype=KDA_BF16, scale=0.0, lower_bound=0.0, flags=0,
-              rows_per_workgroup=0, segment_chunks=0, trace_events=None):
+              rows_per_workgroup=0, segment_chunks=0, checkpoint_every=0,
+              checkpoint_rows=0, state_checkpoints=None, checkpoint_cu_starts=None,
+              trace_events=None):
     """Fill a kda_prefill_args from raw pointers (ints), tensors or None."""
     a = kda_prefill_args()
     a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
@@ -207,6 +219,10 @@ def make_args(*, q=None, k=None, v=None, g=None, beta=None, state_in=None, cu_se
     a.flags = int(flags)
     a.rows_per_workgroup = int(rows_per_workgroup)
     a.segment_chunks = int(segment_chunks)
+    a.checkpoint_every = int(checkpoint_every)
+    a.checkpoint_rows = int(checkpoint_rows)
+    a.state_checkpoints = _ptr(state_checkpoints)
+    a.checkpoint_cu_starts = _ptr(checkpoint_cu_starts)
     if trace_events is not None:
         arr = (ctypes.c_void_p * len(trace_events))(*trace_events)
         a._trace_keepalive = arr
@@ -245,6 +261,7 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                 A_log=None, dt_bias=None, lower_bound=None, l2norm_qk=False,
                 beta_is_logit=False, output_final_state=True, state_dtype=None, o=None,
                 state_out=None, workspace=None, rows_per_workgroup=0, segment_chunks=0,
+                checkpoint_every=0, state_checkpoints=None, checkpoint_cu_starts=None,
                 stream=None, trace_events=None):
     """Chunkwise KDA prefill forward on the current (or given) HIP stream.
 
@@ -252,7 +269,14 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
     state_in: [N, H, 128, 128] or None. cu_seqlens: int64 [N + 1] (B = 1) or None.
     A_log / dt_bias / lower_bound: enable the in-kernel gate. Pass state_out=state_in for
     an in-place state update. segment_chunks: 0 automatic, negative serial, positive
-    the time-segment length in chunks. Returns (o, state_out or None).
+    the time-segment length in chunks.
+    checkpoint_every (tokens, a multiple of 16): also write the state before each
+    interval of every sequence (the flashinfer page's checkpoint contract) into
+    state_checkpoints [C, H, 128, 128] at rows checkpoint_cu_starts[n] + r. When the
+    offsets or the buffer are not given they are derived here from the sequence lengths
+    (which reads cu_seqlens back to the host).
+    Returns (o, state_out or None), or (o, state_out or None, state_checkpoints) with
+    checkpoints.
     """
     import torch
 
@@ -281,13 +305,32 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
         o = torch.empty_like(v)
     if state_out is None and output_final_state:
         state_out = torch.empty((N, H, D, D), dtype=state_dtype, device=q.device)
+    if checkpoint_every:
+        if checkpoint_cu_starts is None:
+            if cu_seqlens is None:
+                lens = [T] * B
+            else:
+                cu = cu_seqlens.cpu().tolist()
+                lens = [b - a for a, b in zip(cu[:-1], cu[1:])]
+            every = int(checkpoint_every)
+            counts = [(n + every - 1) // every if every > 0 else 0 for n in lens]
+            starts = [0]
+            for c in counts:
+                starts.append(starts[-1] + c)
+            checkpoint_cu_starts = torch.tensor(starts, dtype=torch.int64, device=q.device)
+        if state_checkpoints is None:
+            rows = int(checkpoint_cu_starts[-1].item())
+            state_checkpoints = torch.empty((rows, H, D, D), dtype=state_dtype, device=q.device)
     args = make_args(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in,
                      cu_seqlens=cu_seqlens, A_log=A_log, dt_bias=dt_bias, o=o,
                      state_out=state_out, B=B, T=T, H=H, N=N, D=D, io_dtype=io,
                      state_dtype=st, scale=0.0 if scale is None else scale,
                      lower_bound=0.0 if lower_bound is None else lower_bound,
                      flags=flags, rows_per_workgroup=rows_per_workgroup,
-                     segment_chunks=segment_chunks, trace_events=trace_events)
+                     segment_chunks=segment_chunks, checkpoint_every=checkpoint_every,
+                     checkpoint_rows=0 if state_checkpoints is None else state_checkpoints.shape[0],
+                     state_checkpoints=state_checkpoints,
+                     checkpoint_cu_starts=checkpoint_cu_starts, trace_events=trace_events)
     need = kda_prefill_workspace_bytes(args)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -296,4 +339,6 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     _raise_if(lib.kda_prefill(ctypes.byref(args), stream))
+    if checkpoint_every:
+        return o, state_out, state_checkpoints
     return o, state_out

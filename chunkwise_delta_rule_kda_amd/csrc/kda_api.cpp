@@ -90,6 +90,11 @@ kda_status check_shape(const kda_prefill_args* a) {
     return fail(KDA_ERR_CONFIG, "rows_per_workgroup %d", a->rows_per_workgroup);
   if (a->segment_chunks > (1 << 24))
     return fail(KDA_ERR_CONFIG, "segment_chunks %d", a->segment_chunks);
+  if (a->checkpoint_every < 0 || a->checkpoint_every % KDA_CHUNK != 0)
+    return fail(KDA_ERR_CONFIG, "checkpoint_every %lld is not a non-negative multiple of 16",
+                (long long)a->checkpoint_every);
+  if (a->checkpoint_rows < 0)
+    return fail(KDA_ERR_CONFIG, "checkpoint_rows %lld", (long long)a->checkpoint_rows);
   return KDA_OK;
 }
 
@@ -265,11 +270,15 @@ kda_status kda_prefill_check(const kda_prefill_args* a) {
     if (reinterpret_cast<uintptr_t>(a->workspace) % 256)
       return fail(KDA_ERR_WORKSPACE, "workspace not 256-byte aligned");
   }
+  const bool ckpt = a->checkpoint_every > 0;
+  if (ckpt && (!a->state_checkpoints || !a->checkpoint_cu_starts))
+    return fail(KDA_ERR_NULL, "checkpoints need state_checkpoints and checkpoint_cu_starts");
   // Alignment the kernels' vector accesses rely on.
-  const void* vec[] = {a->q, a->k, a->v, a->g, a->o, a->state_in, a->state_out};
+  const void* vec[] = {a->q, a->k, a->v, a->g, a->o, a->state_in, a->state_out,
+                       ckpt ? a->state_checkpoints : nullptr};
   for (const void* p : vec)
     if (reinterpret_cast<uintptr_t>(p) % 16)
-      return fail(KDA_ERR_SHAPE, "q, k, v, g, o and state pointers must be 16-byte aligned");
+      return fail(KDA_ERR_SHAPE, "q, k, v, g, o, state and checkpoint pointers must be 16-byte aligned");
 
   const Range ins[] = {
       range_of(a->q, tensor, "q"),          range_of(a->k, tensor, "k"),
@@ -278,6 +287,7 @@ kda_status kda_prefill_check(const kda_prefill_args* a) {
       range_of(a->cu_seqlens, a->cu_seqlens ? (a->N + 1) * 8 : 0, "cu_seqlens"),
       range_of(a->A_log, (a->flags & KDA_FLAG_GATE_IN_KERNEL) ? a->H * 4 : 0, "A_log"),
       range_of(a->dt_bias, (a->flags & KDA_FLAG_GATE_IN_KERNEL) ? a->H * 512 : 0, "dt_bias"),
+      range_of(a->checkpoint_cu_starts, ckpt ? (a->N + 1) * 8 : 0, "checkpoint_cu_starts"),
   };
   const Range o = range_of(a->o, tensor, "o");
   const Range so = range_of(a->state_out, state_b, "state_out");
@@ -293,6 +303,16 @@ kda_status kda_prefill_check(const kda_prefill_args* a) {
   if (overlap(o, so)) return fail(KDA_ERR_ALIAS, "o overlaps state_out");
   if (overlap(o, ws)) return fail(KDA_ERR_ALIAS, "o overlaps workspace");
   if (overlap(so, ws)) return fail(KDA_ERR_ALIAS, "state_out overlaps workspace");
+  if (ckpt) {
+    const Range ck = range_of(a->state_checkpoints,
+                              static_cast<size_t>(a->checkpoint_rows) * a->H * KDA_HEAD_DIM *
+                                  KDA_HEAD_DIM * elem_size(a->state_dtype),
+                              "state_checkpoints");
+    for (const Range& in : ins)
+      if (overlap(ck, in)) return fail(KDA_ERR_ALIAS, "state_checkpoints overlaps %s", in.name);
+    if (overlap(ck, o) || overlap(ck, so) || overlap(ck, ws))
+      return fail(KDA_ERR_ALIAS, "state_checkpoints overlaps an output or the workspace");
+  }
   return KDA_OK;
 }
 
@@ -360,6 +380,12 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   p.seg_len = pl.seg_len;
   p.segs_per_seq = pl.segs_per_seq;
   p.seg_stride = pl.seg_stride;
+  if (a->checkpoint_every > 0) {
+    p.ckpt = a->state_checkpoints;
+    p.ckpt_cu = a->checkpoint_cu_starts;
+    p.ckpt_every = a->checkpoint_every / KDA_CHUNK;
+    p.ckpt_rows = a->checkpoint_rows;
+  }
   if (pl.seg_len > 0) {
     p.scan_s = reinterpret_cast<float*>(ws + pl.scan_s);
     p.scan_phi = reinterpret_cast<unsigned short*>(ws + pl.scan_phi);

@@ -55,6 +55,11 @@ struct Params {
   int64_t* cu_segs;           // varlen: [N + 1] prefix of segments per sequence
   float* scan_s;              // FP32 [H][seg_stride][128][128]: S_p, Z_p
   unsigned short* scan_phi;   // BF16 [H][seg_stride][128 keys][128 rows]: Phi_p transposed
+  // State checkpoints (ckpt_every chunks apart; 0 = none).
+  void* ckpt;                 // [ckpt_rows][H][128][128] of the state dtype
+  const int64_t* ckpt_cu;     // [N + 1] row offsets
+  int64_t ckpt_every;         // chunks between checkpoints
+  int64_t ckpt_rows;
 };
 
 hipError_t launch_plan(const Params& p, hipStream_t stream);

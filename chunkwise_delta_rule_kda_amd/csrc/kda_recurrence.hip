@@ -122,6 +122,8 @@ struct Task {
   int64_t nch;        // chunks in the run
   int64_t sh;         // sequence * H + head
   int64_t h;
+  int64_t n;          // sequence
+  int64_t c0s;        // chunk index of the run's first chunk within its sequence
   int vwg;            // first row of the workgroup within its 128-row space
   int start;          // StartKind
   bool vzero;         // V = 0 (rows of Phi)
@@ -197,6 +199,8 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
     t.nch = nch;
     t.sh = sh;
     t.h = sh - n * H;
+    t.n = n;
+    t.c0s = 0;
     t.vwg = blk * rows;
     t.start = kStartIn;
     return true;
@@ -282,6 +286,8 @@ __device__ bool segment_task(const Params& p, Task& t, int64_t h, int64_t n, int
   t.nch = c1 > c0 ? c1 - c0 : 0;
   t.sh = n * H + h;
   t.h = h;
+  t.n = n;
+  t.c0s = c0;
   const int64_t slot = h * p.seg_stride + gsg;  // scan slot of this segment
   if (p.mode == kModeScanA) {
     if (vr < kD) {
@@ -528,7 +534,10 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
     if (rest > 2) step(IntC<3>{}, c0 + 2);
 }
 
-template <bool BF16IO, bool BF16ST, int W, bool OUT>
+// OUT: the run writes O (and carries the true state); CKPT: it also writes state
+// checkpoints (a separate instantiation, so that runs without them keep a loop body
+// with no checkpoint test in it).
+template <bool BF16IO, bool BF16ST, int W, bool OUT, bool CKPT>
 __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds_u8* ring,
                                              int wave, int lane) {
   using T = Tile<BF16IO, W>;
@@ -578,9 +587,29 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
     };
     TailIn tail;
     read_tail<OUT>(tail, ring, lane);
+    // State checkpoints (runs that write O are the runs that carry the true state): the
+    // state before every chunk j of the sequence with j % ckpt_every == 0 goes to row
+    // ckpt_cu[n] + j / ckpt_every, if that row exists.
+    const int64_t ck_q = CKPT ? p.ckpt_every : 1;
+    int64_t ck_c = 0, ck_row = 0;
+    if constexpr (CKPT) {
+      ck_c = (ck_q - t.c0s % ck_q) % ck_q;
+      ck_row = p.ckpt_cu[t.n] + (t.c0s + ck_c) / ck_q;
+    }
 #pragma unroll 1
     for (int64_t c = 0; c < nch; ++c) {
       const int ns = cs + 1 == kSlots ? 0 : cs + 1;  // slot of chunk c + 1
+      if constexpr (CKPT) {
+        if (c == ck_c) {
+          if (ck_row >= 0 && ck_row < p.ckpt_rows) {
+            const int64_t crow = ((ck_row * p.H + t.h) * kD + v0 + m) * kD;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) store4<BF16ST>(p.ckpt, crow + 16 * b + 4 * grp, st[b]);
+          }
+          ck_c += ck_q;
+          ++ck_row;
+        }
+      }
       read_barrier();  // B_c: chunk c + 1 visible
       // All of chunk c + 1's operands are read here, one chunk ahead, so that their
       // latency (they queue behind the loaders' writes of chunk c + 2) is hidden by
@@ -625,7 +654,9 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
   }
 }
 
-template <bool BF16IO, bool BF16ST, int W>
+// CK: the instantiation that writes state checkpoints, launched only when they are
+// asked for (kept apart so that the common kernel's code is unaffected by it).
+template <bool BF16IO, bool BF16ST, int W, bool CK>
 // At most two waves per SIMD (256 registers each): with more room the compiler keeps
 // the state in AGPRs and copies it through VGPRs every chunk for the decay multiply.
 __global__ __launch_bounds__(block_threads(W), 2) void kda_recurrence_kernel(Params p) {
@@ -641,10 +672,10 @@ __global__ __launch_bounds__(block_threads(W), 2) void kda_recurrence_kernel(Par
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int lt = static_cast<int>(threadIdx.x) - 64 * W;
   if (t.out) {
-    if (wave < W) compute_loop<BF16IO, BF16ST, W, true>(p, t, ring, wave, lane);
+    if (wave < W) compute_loop<BF16IO, BF16ST, W, true, CK>(p, t, ring, wave, lane);
     else if (t.nch > 0) loader_loop<BF16IO, T, true>(p, t, ring, lt);
   } else {
-    if (wave < W) compute_loop<BF16IO, BF16ST, W, false>(p, t, ring, wave, lane);
+    if (wave < W) compute_loop<BF16IO, BF16ST, W, false, false>(p, t, ring, wave, lane);
     else if (t.nch > 0) loader_loop<BF16IO, T, false>(p, t, ring, lt);
   }
 }
@@ -759,22 +790,28 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   if (s + 1 <= last) step(IntC<1>{}, s + 1);
 }
 
-template <bool BF16IO, bool BF16ST>
-void launch_io(const Params& p, dim3 grid, hipStream_t stream) {
+template <bool BF16IO, bool BF16ST, bool CK>
+void launch_waves(const Params& p, dim3 grid, hipStream_t stream) {
   switch (p.waves) {
     case 1:
-      hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 1>), grid,
+      hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 1, CK>), grid,
                          dim3(Tile<BF16IO, 1>::NT), 0, stream, p);
       break;
     case 2:
-      hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 2>), grid,
+      hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 2, CK>), grid,
                          dim3(Tile<BF16IO, 2>::NT), 0, stream, p);
       break;
     default:
-      hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 4>), grid,
+      hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 4, CK>), grid,
                          dim3(Tile<BF16IO, 4>::NT), 0, stream, p);
       break;
   }
+}
+
+template <bool BF16IO, bool BF16ST>
+void launch_io(const Params& p, dim3 grid, hipStream_t stream) {
+  if (p.ckpt_every > 0) launch_waves<BF16IO, BF16ST, true>(p, grid, stream);
+  else launch_waves<BF16IO, BF16ST, false>(p, grid, stream);
 }
 
 }  // namespace

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 #define KDA_HEAD_DIM 128 /* d_k = d_v = 128 */
 #define KDA_CHUNK 16     /* tokens per chunk */
 
@@ -63,8 +63,9 @@ typedef enum kda_status {
   KDA_ERR_WORKSPACE = 7,  /* workspace NULL, too small or not 256-byte aligned */
   KDA_ERR_HIP = 8,        /* a HIP runtime call or kernel launch failed */
   KDA_ERR_CU_SEQLENS = 9, /* kda_debug_check_cu_seqlens found a contract violation */
-  KDA_ERR_CONFIG = 10     /* rows_per_workgroup not 0, 16, 32 or 64, or segment_chunks
-                             above 2^24 */
+  KDA_ERR_CONFIG = 10     /* rows_per_workgroup not 0, 16, 32 or 64, segment_chunks
+                             above 2^24, checkpoint_every not a multiple of 16 (or
+                             negative), or checkpoint_rows negative */
 } kda_status;
 
 enum {
@@ -129,6 +130,24 @@ typedef struct kda_prefill_args {
      serial run per sequence); positive = this many chunks per segment. Results differ
      from the serial form only by rounding. */
   int32_t segment_chunks;
+
+  /* State checkpoints, as in the "flashinfer.kda_prefill" page's contract (section
+     "State and graph semantics"). checkpoint_every: the interval in tokens, a positive
+     multiple of 16, or 0 (no checkpoints). When set, every non-empty sequence n writes
+     ceil(len_n / checkpoint_every) states, the states before each interval: row
+     checkpoint_cu_starts[n] + r of state_checkpoints holds the state after
+     r * checkpoint_every tokens of the sequence (r = 0: its initial state). An empty
+     sequence writes none.
+     state_checkpoints: [checkpoint_rows, H, 128 (values), 128 (keys)] of state_dtype,
+     device, 16-byte aligned, write only, must not overlap any other buffer.
+     checkpoint_cu_starts: int64 [N + 1] device, the caller's row offsets (on the page's
+     contract, cu[0] = 0 and cu[n + 1] - cu[n] = ceil(len_n / checkpoint_every); they
+     are device data and not checked on the host). Rows at or beyond checkpoint_rows are
+     never written, whatever the offsets say. */
+  int64_t checkpoint_every;
+  int64_t checkpoint_rows;
+  void *state_checkpoints;
+  const int64_t *checkpoint_cu_starts;
 
   /* Optional timing hooks (host array of hipEvent_t handles, or NULL). When
      n_trace_events >= 3, the library records trace_events[0] before the first kernel,

@@ -41,7 +41,8 @@ def to_device(x: kda_synth.KdaInputs, device="cuda"):
 
 
 def run_gpu(x, **kw):
-    """Returns (o, state_out) as float64 numpy arrays plus the raw torch outputs."""
+    """Returns (o, state_out) as float64 numpy arrays plus the raw torch outputs (o, state_out
+    and, with checkpoint_every, the checkpoints)."""
     import torch
 
     import chunkwise_delta_rule_kda_amd as kda
@@ -49,11 +50,12 @@ def run_gpu(x, **kw):
     d = to_device(x)
     d.update(kw)
     q, k, v, g, beta = d.pop("q"), d.pop("k"), d.pop("v"), d.pop("g"), d.pop("beta")
-    o, st = kda.kda_prefill(q, k, v, g, beta, **d)
+    raw = kda.kda_prefill(q, k, v, g, beta, **d)  # (o, state[, checkpoints])
+    o, st = raw[0], raw[1]
     torch.cuda.synchronize()
     on = o.float().cpu().numpy().astype(np.float64)
     sn = None if st is None else st.float().cpu().numpy().astype(np.float64)
-    return on, sn, (o, st)
+    return on, sn, raw
 
 
 def run_oracle(x, heads=None):

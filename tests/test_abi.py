@@ -47,7 +47,7 @@ def test_record_size_matches_header():
 
 def test_abi_version_and_status_strings():
     lib = kda.load_library()
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     for code in range(11):
         assert kda.kda_status_string(code) and kda.kda_status_string(code) != "unknown status"
     assert kda.kda_status_string(99) == "unknown status"
@@ -135,6 +135,24 @@ def test_workspace_checks():
     # (cu_chunks and cu_segs, 2 (N + 1) int64)
     v = fake(T=100, H=3, N=5, varlen=True)
     assert kda.kda_prefill_workspace_bytes(v) == 256 + ((100 + 15 * 5) // 16) * 3 * kda.KDA_WS_RECORD
+
+
+def test_checkpoint_validation():
+    base = 0x7F0000000000
+    ck = dict(checkpoint_every=32, checkpoint_rows=4, state_checkpoints=base + 10 * 256 * MB,
+              checkpoint_cu_starts=base + 11 * 256 * MB)
+    assert status(fake(**ck)) == 0
+    assert status(fake(**dict(ck, checkpoint_every=8))) == 10      # not a multiple of 16
+    assert status(fake(**dict(ck, checkpoint_every=-16))) == 10
+    assert status(fake(**dict(ck, checkpoint_rows=-1))) == 10
+    assert status(fake(**dict(ck, state_checkpoints=None))) == 1
+    assert status(fake(**dict(ck, checkpoint_cu_starts=None))) == 1
+    assert status(fake(**dict(ck, state_checkpoints=base + 10 * 256 * MB + 8))) == 2
+    assert status(fake(**dict(ck, state_checkpoints=base + 2 * 256 * MB))) == 6   # == v
+    assert status(fake(**dict(ck, state_checkpoints=base + 6 * 256 * MB))) == 6   # == o
+    assert status(fake(**dict(ck, checkpoint_cu_starts=base + 10 * 256 * MB))) == 6
+    # Off: the checkpoint pointers are ignored.
+    assert status(fake(checkpoint_every=0, state_checkpoints=base + 2 * 256 * MB)) == 0
 
 
 def test_misaligned_vector_pointer_rejected():
