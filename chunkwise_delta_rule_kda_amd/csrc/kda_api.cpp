@@ -334,7 +334,7 @@ kda_status kda_prefill_plan(const kda_prefill_args* a, int32_t num_cus, kda_plan
   if (pl.seg_len > 0) {
     out->recurrence_workgroups = scan_a_workgroups(a, pl, rows);
     out->scan_c_workgroups = scan_c_workgroups(a, pl, rows);
-    out->combine_workgroups = a->H * a->N * 8;
+    out->combine_workgroups = (a->H * a->N + 7) / 8 * 64;
   } else {
     out->recurrence_workgroups = a->N * a->H * (KDA_HEAD_DIM / rows);
   }

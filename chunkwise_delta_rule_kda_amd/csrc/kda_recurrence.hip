@@ -104,12 +104,16 @@ struct Tile {
   static_assert(kSlots * SLOT <= 65536, "LDS ring");
 };
 
-// Column of row r of Phi in its stored transpose: r = 32 kk + 16 h + 4 grp + i (the key
-// order of the MFMA operands) is stored at 32 kk + 8 grp + 4 h + i, so that the eight
-// entries one lane of the combine needs for one 16x16x32 product are contiguous.
-__device__ __forceinline__ int phi_col(int r) {
-  const int kk = r >> 5, h = (r >> 4) & 1, grp = (r >> 2) & 3, i = r & 3;
-  return 32 * kk + 8 * grp + 4 * h + i;
+// Scan slots hold MFMA fragments, so that every access to them is one contiguous 1 KB
+// piece per wave instruction:
+// - states (FP32, 128 x 128): [row block rb 8][key block b 8][lane 64][4], lane
+//   L = 16 grp + m holding S[16 rb + m][16 b + 4 grp + j] (the accumulator layout);
+// - transitions Phi^T (BF16, 128 x 128): [output key block b 8][key group kk 4][lane
+//   64][8], lane L = 16 grp + m holding Phi[k][16 b + m] for the eight keys
+//   k = 32 kk + 16 (e / 4) + 4 grp + e % 4 (the 16x16x32 A-operand layout; Phi^T is the
+//   A operand of the combine).
+__device__ __forceinline__ int64_t state_frag(int rb, int b, int lane) {
+  return ((rb * 8 + b) * 64 + lane) * 4;  // in floats
 }
 
 // Where one workgroup's run starts, what it reads and what it writes.
@@ -548,7 +552,6 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
 
   // State rows v0 + m, keys 16 b + 4 grp + j: the 16x16x16 accumulator layout.
   const int64_t srow = (t.sh * kD + v0 + m) * kD;
-  const int64_t lrow = (v0 + m) * kD;  // row in a scan slot
   f32x4 st[8];
   bf16x8 sp[4];
 #pragma unroll
@@ -557,7 +560,7 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
     if (t.start == kStartIn && p.state_in) {
       st[b] = load4<BF16ST>(p.state_in, srow + key);
     } else if (t.start == kStartScan) {
-      st[b] = load4<false>(t.s_src, lrow + key);
+      st[b] = load4<false>(t.s_src, state_frag(v0 >> 4, b, lane));
     } else if (t.start == kStartIdentity) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) st[b][j] = (v0 + m == key + j) ? 1.f : 0.f;
@@ -642,15 +645,22 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
   }
   if (t.s_dst) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) store4<false>(t.s_dst, lrow + 16 * b + 4 * grp, st[b]);
+    for (int b = 0; b < 8; ++b) store4<false>(t.s_dst, state_frag(v0 >> 4, b, lane), st[b]);
   }
-  if (t.phi_dst) {  // transposed, [key][phi_col(row)]
-    const int col = phi_col(v0 + m);
+  if (t.phi_dst) {
+    // This lane holds Phi[r][16 b + 4 grp + j] for row r = v0 + m: key r of output
+    // key 16 b + m' (m' = 4 grp + j) sits in group kk = r / 32, lane 16 grp' + m',
+    // element e with r % 32 = 16 (e / 4) + 4 grp' + e % 4.
+    const int r = v0 + m;
+    const int kk = r >> 5, q = r & 31;
+    const int e = 4 * (q >> 4) + (q & 3);
+    const int grpp = (q & 15) >> 2;
 #pragma unroll
     for (int b = 0; b < 8; ++b)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        t.phi_dst[(16 * b + 4 * grp + j) * kD + col] = float_to_bf16_bits(st[b][j]);
+        t.phi_dst[((b * 4 + kk) * 64 + 16 * grpp + 4 * grp + j) * 8 + e] =
+            float_to_bf16_bits(st[b][j]);
   }
 }
 
@@ -683,14 +693,13 @@ __global__ __launch_bounds__(block_threads(W), 2) void kda_recurrence_kernel(Par
 // Launch B of the segmented form: S_{p+1} = S_p Phi_p + Z_p, p = 1 .. P-2, for 16 value
 // rows of one (sequence, head) per workgroup. In the transposed form S^T_{p+1} =
 // Phi_p^T S_p^T + Z_p^T; wave w computes output key blocks 2 w and 2 w + 1 (eight
-// 16x16x32 products). Phi_p^T, stored [key][phi_col(row)] by launch A, is the A operand:
-// each lane's eight operands of one product are one 16-byte global load, and a wave's
-// slice of Phi (32 keys x 128) is read by that wave alone, so it goes straight to
-// registers, three steps ahead together with Z. The new state, packed to BF16, is the B
+// 16x16x32 products). Phi_p^T, stored as A-operand fragments by launch A, is the A
+// operand: one 1 KB contiguous load per wave and product, and a wave's slice of Phi
+// (32 keys x 128) is read by that wave alone, so it goes straight to registers, three
+// steps ahead together with Z (state fragments, like S). The new state, packed to BF16, is the B
 // operand of the next step; the waves exchange their packed blocks through LDS.
 // Per step a workgroup moves 32 KB of Phi, 8 KB of Z and 8 KB of S: the per-CU stream
 // rate, not the products, sets the step time, hence 16 rows (8 workgroups) per pair.
-constexpr int kCombineRows = 16;
 constexpr int kCombineDepth = 3;  // steps of Phi and Z in flight per wave
 
 struct CombineIn {
@@ -701,9 +710,12 @@ struct CombineIn {
 __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) unsigned char xch_[2 * 4 * 64 * 16];
   lds_u8* xbase = (lds_u8*)(xch_);  // address-space cast
-  const int64_t task = blockIdx.x;  // (h * N + n) * 8 + row block
-  const int rb = static_cast<int>(task & 7);
-  const int64_t hn = task >> 3;
+  // Workgroup b runs on XCD b % 8. The 8 row blocks of one (sequence, head) pair read
+  // the same Phi, so they go to one XCD: pair hn = 8 group + (b % 8), row block
+  // (b / 8) % 8, group b / 64. Pairs past H N exit.
+  const int64_t b = blockIdx.x;
+  const int rb = static_cast<int>((b >> 3) & 7);
+  const int64_t hn = (b >> 6) * 8 + (b & 7);
   const int64_t h = hn / p.N;
   const int64_t n = hn - h * p.N;
   if (h >= p.H) return;
@@ -712,18 +724,14 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   if (nseg < 3 || first < 0 || first + nseg > p.seg_stride) return;  // nothing to combine
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & 63;
-  const int m = lane & 15;
-  const int grp = lane >> 4;
-  const int64_t lrow = (kCombineRows * rb + m) * kD;
   const int64_t slot0 = h * p.seg_stride + first;
   float* sbase = p.scan_s + slot0 * (kD * kD);
   const unsigned char* pbase = reinterpret_cast<const unsigned char*>(p.scan_phi + slot0 * (kD * kD));
   const int64_t last = nseg - 2;  // steps s = 1 .. last
-  // This lane's operand offsets: Phi^T row 16 b + m, bytes 64 kk + 16 grp; Z / S keys
-  // 16 b + 4 grp (b = 2 wave + i).
-  const int koff0 = 16 * (2 * wave) + 4 * grp;
-  const int koff1 = koff0 + 16;
-  const int aoff = (16 * (2 * wave) + m) * (kD * 2) + 16 * grp;
+  // This lane's fragment offsets: output key blocks b = 2 wave + i of row block rb.
+  const int64_t koff0 = state_frag(rb, 2 * wave, lane);
+  const int64_t koff1 = state_frag(rb, 2 * wave + 1, lane);
+  const int aoff = (2 * wave * 4 * 64 + lane) * 16;  // bytes: block 2 wave, group 0
 
   auto fetch = [&](CombineIn& x, int64_t s) {
     s = s < last ? s : last;  // past the last step: re-read it (in bounds, unused)
@@ -732,8 +740,8 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        x.a[i][kk] = *reinterpret_cast<const u32x4*>(ph + i * 16 * (kD * 2) + 64 * kk);
-    const float* z = sbase + (s + 1) * (kD * kD) + lrow;  // Z_s lives in slot s + 1
+        x.a[i][kk] = *reinterpret_cast<const u32x4*>(ph + (i * 4 + kk) * 1024);
+    const float* z = sbase + (s + 1) * (kD * kD);  // Z_s lives in slot s + 1
     x.z[0] = load4<false>(z, koff0);
     x.z[1] = load4<false>(z, koff1);
   };
@@ -745,7 +753,7 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
 
   f32x4 st[2];
   {
-    const float* s1 = sbase + 1 * (kD * kD) + lrow;
+    const float* s1 = sbase + 1 * (kD * kD);
     st[0] = load4<false>(s1, koff0);
     st[1] = load4<false>(s1, koff1);
   }
@@ -773,7 +781,7 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
       st[i] = acc + in[set].z[i];
     }
     *xch((s + 1) & 1, wave) = pack8(st[0], st[1]);
-    float* out = sbase + (s + 1) * (kD * kD) + lrow;  // S_{s+1} replaces Z_s
+    float* out = sbase + (s + 1) * (kD * kD);  // S_{s+1} replaces Z_s
     store4<false>(out, koff0, st[0]);
     store4<false>(out, koff1, st[1]);
     fetch(in[set], s + kCombineDepth);
@@ -836,7 +844,7 @@ hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16, 
 }
 
 hipError_t launch_combine(const Params& p, hipStream_t stream) {
-  const int64_t wgs = p.H * p.N * (kD / kCombineRows);
+  const int64_t wgs = (p.H * p.N + 7) / 8 * 64;  // 8 row blocks per pair, pairs by XCD
   if (wgs <= 0) return hipSuccess;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kda_combine_kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream,

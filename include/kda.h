@@ -173,11 +173,16 @@ typedef struct kda_prefill_args {
  *                                 over all sequences in order and max_chunks is the
  *                                 plan's bound (kda_prefill_plan): N * ceil(T / 16)
  *                                 for the fixed layout, (T + 15 N) / 16 for varlen.
- *   scan_state_offset             segmented form only: FP32 [H][S][128][128], the
- *                                 start state (or zero-start end state) per segment,
- *                                 S = segments_per_head_bound.
- *   scan_transition_offset        segmented form only: BF16 [H][S][128][128], each
- *                                 middle segment's transition, stored transposed.
+ *   scan_state_offset             segmented form only: FP32 [H][S] slots of 128 x 128,
+ *                                 the start state (or zero-start end state) per
+ *                                 segment, S = segments_per_head_bound; inside a slot,
+ *                                 MFMA fragments [row block 8][key block 8][lane 64][4]
+ *                                 with lane 16 g + m holding S[16 rb + m][16 b + 4 g + j].
+ *   scan_transition_offset        segmented form only: BF16 [H][S] slots of 128 x 128,
+ *                                 each middle segment's transition Phi, as fragments
+ *                                 [key block 8][key group 4][lane 64][8] with lane
+ *                                 16 g + m holding Phi[k][16 b + m] for the keys
+ *                                 k = 32 kk + 16 (e / 4) + 4 g + e % 4.
  * KDA_WS_HEADER = round_up((N + 1) * 16, 256) for varlen, 0 for the fixed layout.
  *
  * A record holds, for the chunk's 16 tokens (pad tokens of a short last chunk behave as

@@ -181,7 +181,7 @@ def test_plan_segments_small_head_counts():
     # transition (Phi) rows of segments 1 .. 10; launch C re-runs segments 1 .. 11.
     assert p["recurrence_workgroups"] == 6 * (2 + 4 * 10)
     assert p["scan_c_workgroups"] == 6 * 11 * 2
-    assert p["combine_workgroups"] == 6 * 8
+    assert p["combine_workgroups"] == 64  # 8 row blocks x 6 pairs, padded to 8 XCDs
     records = 512 * 6 * kda.KDA_WS_RECORD
     assert p["scan_state_offset"] == records            # already 256-byte aligned
     slots = 6 * 12
