@@ -87,6 +87,15 @@ struct IntC {
   static constexpr int value = V;
 };
 
+// f(IntC<0>), ..., f(IntC<N - 1>), in order.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    unroll<N, I + 1>(f);
+  }
+}
+
 template <bool BF16IO, int W>
 struct Tile {
   static constexpr int NL = loader_waves(W);              // loader waves
@@ -100,7 +109,7 @@ struct Tile {
   static constexpr int DEPTH = K <= 5 ? 4 : 3;            // chunks in flight per loader
   static constexpr int SLOT = K * LT * 16;                // padded ring slot
   static_assert(K * (DEPTH - 1) <= 63, "vmcnt range");
-  static_assert(DEPTH == 3 || DEPTH == 4, "loader unrolling");
+  static_assert(DEPTH >= 2, "loader pipeline");
   static_assert(kSlots * SLOT <= 65536, "LDS ring");
 };
 
@@ -525,17 +534,13 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
   };
   int64_t c0 = 0;
 #pragma unroll 1
-  for (; c0 + T::DEPTH <= nch; c0 += T::DEPTH) {
-    step(IntC<1 % T::DEPTH>{}, c0);
-    step(IntC<2 % T::DEPTH>{}, c0 + 1);
-    step(IntC<3 % T::DEPTH>{}, c0 + 2);
-    if constexpr (T::DEPTH == 4) step(IntC<0>{}, c0 + 3);
-  }
+  for (; c0 + T::DEPTH <= nch; c0 += T::DEPTH)
+    unroll<T::DEPTH>([&](auto d) { step(IntC<(decltype(d)::value + 1) % T::DEPTH>{}, c0 + decltype(d)::value); });
   const int64_t rest = nch - c0;  // 0 .. DEPTH - 1
-  if (rest > 0) step(IntC<1 % T::DEPTH>{}, c0);
-  if (rest > 1) step(IntC<2 % T::DEPTH>{}, c0 + 1);
-  if constexpr (T::DEPTH == 4)
-    if (rest > 2) step(IntC<3>{}, c0 + 2);
+  unroll<T::DEPTH - 1>([&](auto d) {
+    constexpr int i = decltype(d)::value;
+    if (rest > i) step(IntC<(i + 1) % T::DEPTH>{}, c0 + i);
+  });
 }
 
 // OUT: the run writes O (and carries the true state); CKPT: it also writes state
