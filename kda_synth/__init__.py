@@ -218,3 +218,29 @@ def with_dtype(x: KdaInputs, dtype):
     f = lambda a: None if a is None else _store(a, dtype)
     return replace(x, q=f(x.q), k=f(x.k), v=f(x.v), g=f(x.g), beta=f(x.beta),
                    state0=f(x.state0), dtype=dtype, state_dtype=dtype)
+
+
+def large_device(*, B, T, H, seed, device="cuda"):
+    """Config 1's recipe (q, k ~ N(0,1) at unit L2 norm per row, v ~ N(0,1),
+    g = -5 logistic(N(0,1)), beta = logistic(N(0,1)), zero initial state), drawn on the
+    GPU with a seeded torch generator in FP32 and stored as BF16: for shapes too large
+    to draw on the host. Returns a dict of device tensors q, k, v, g, beta
+    ([B, T, H, 128] / [B, T, H]); the oracle is fed host copies of the heads it checks.
+    """
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    shp = (B, T, H, D)
+    out = {}
+    for name in ("q", "k", "v", "g"):
+        x = torch.randn(shp, generator=gen, device=device, dtype=torch.float32)
+        if name in ("q", "k"):
+            x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        elif name == "g":
+            x = -5.0 * torch.sigmoid(x)
+        out[name] = x.to(torch.bfloat16)
+        del x
+    b = torch.randn((B, T, H), generator=gen, device=device, dtype=torch.float32)
+    out["beta"] = torch.sigmoid(b).to(torch.bfloat16)
+    return out
