@@ -97,6 +97,10 @@ class kda_prefill_args(ctypes.Structure):
         ("checkpoint_rows", ctypes.c_int64),
         ("state_checkpoints", ctypes.c_void_p),
         ("checkpoint_cu_starts", ctypes.c_void_p),
+        ("ssm_state_indices", ctypes.c_void_p),
+        ("state_pool_slots", ctypes.c_int64),
+        ("state_slot_pitch", ctypes.c_int64),
+        ("seq_order", ctypes.c_void_p),
         ("trace_events", ctypes.c_void_p),
         ("n_trace_events", ctypes.c_int32),
     ]
@@ -119,7 +123,7 @@ class kda_plan_info(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 3  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
+ABI_VERSION = 4  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
 
 
 def lib_path():
@@ -202,6 +206,7 @@ def make_args(*, q=None, k=None, v=None, g=None, beta=None, state_in=None, cu_se
               state_dtype=KDA_BF16, scale=0.0, lower_bound=0.0, flags=0,
               rows_per_workgroup=0, segment_chunks=0, checkpoint_every=0,
               checkpoint_rows=0, state_checkpoints=None, checkpoint_cu_starts=None,
+              ssm_state_indices=None, state_pool_slots=0, state_slot_pitch=0, seq_order=None,
               trace_events=None):
     """Fill a kda_prefill_args from raw pointers (ints), tensors or None."""
     a = kda_prefill_args()
@@ -223,6 +228,10 @@ def make_args(*, q=None, k=None, v=None, g=None, beta=None, state_in=None, cu_se
     a.checkpoint_rows = int(checkpoint_rows)
     a.state_checkpoints = _ptr(state_checkpoints)
     a.checkpoint_cu_starts = _ptr(checkpoint_cu_starts)
+    a.ssm_state_indices = _ptr(ssm_state_indices)
+    a.state_pool_slots = int(state_pool_slots)
+    a.state_slot_pitch = int(state_slot_pitch)
+    a.seq_order = _ptr(seq_order)
     if trace_events is not None:
         arr = (ctypes.c_void_p * len(trace_events))(*trace_events)
         a._trace_keepalive = arr
@@ -262,7 +271,7 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                 beta_is_logit=False, output_final_state=True, state_dtype=None, o=None,
                 state_out=None, workspace=None, rows_per_workgroup=0, segment_chunks=0,
                 checkpoint_every=0, state_checkpoints=None, checkpoint_cu_starts=None,
-                stream=None, trace_events=None):
+                ssm_state_indices=None, seq_order=None, stream=None, trace_events=None):
     """Chunkwise KDA prefill forward on the current (or given) HIP stream.
 
     q, k, v, g: [B, T, H, 128] bf16 or fp32 CUDA tensors (contiguous); beta [B, T, H].
@@ -275,6 +284,11 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
     state_checkpoints [C, H, 128, 128] at rows checkpoint_cu_starts[n] + r. When the
     offsets or the buffer are not given they are derived here from the sequence lengths
     (which reads cu_seqlens back to the host).
+    ssm_state_indices (int32 [N]): state_in is a pool [N_pool, H, 128, 128] (its first
+    dimension may be padded); sequence n starts from slot ssm_state_indices[n] and its
+    final state is written back there (the returned state is the pool).
+    seq_order (int32 [N], a permutation): the order in which the sequences' workgroups
+    start (decreasing length shortens the last partial wave); results do not change.
     Returns (o, state_out or None), or (o, state_out or None, state_checkpoints) with
     checkpoints.
     """
@@ -303,6 +317,17 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
             raise KdaError(4, "the in-kernel gate needs lower_bound")
     if o is None:
         o = torch.empty_like(v)
+    pool_slots = pool_pitch = 0
+    for name, t in (("ssm_state_indices", ssm_state_indices), ("seq_order", seq_order)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or t.numel() != N):
+            raise KdaError(3, f"{name} must be an int32 CUDA tensor of N={N} entries")
+    if ssm_state_indices is not None:
+        if state_in is None or state_in.dim() != 4 or state_in.shape[1:] != (H, D, D):
+            raise KdaError(2, "a state pool needs state_in [N_pool, H, 128, 128]")
+        if not state_in[0].is_contiguous():
+            raise KdaError(2, "each state pool slot must be contiguous")
+        pool_slots, pool_pitch = state_in.shape[0], state_in.stride(0)
+        state_out = state_in
     if state_out is None and output_final_state:
         state_out = torch.empty((N, H, D, D), dtype=state_dtype, device=q.device)
     if checkpoint_every:
@@ -330,7 +355,10 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                      segment_chunks=segment_chunks, checkpoint_every=checkpoint_every,
                      checkpoint_rows=0 if state_checkpoints is None else state_checkpoints.shape[0],
                      state_checkpoints=state_checkpoints,
-                     checkpoint_cu_starts=checkpoint_cu_starts, trace_events=trace_events)
+                     checkpoint_cu_starts=checkpoint_cu_starts,
+                     ssm_state_indices=ssm_state_indices, state_pool_slots=pool_slots,
+                     state_slot_pitch=pool_pitch, seq_order=seq_order,
+                     trace_events=trace_events)
     need = kda_prefill_workspace_bytes(args)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -95,7 +95,23 @@ kda_status check_shape(const kda_prefill_args* a) {
                 (long long)a->checkpoint_every);
   if (a->checkpoint_rows < 0)
     return fail(KDA_ERR_CONFIG, "checkpoint_rows %lld", (long long)a->checkpoint_rows);
+  if (a->ssm_state_indices) {
+    const int64_t dense = a->H * KDA_HEAD_DIM * KDA_HEAD_DIM;
+    if (!a->state_in) return fail(KDA_ERR_CONFIG, "a state pool needs state_in");
+    if (a->state_pool_slots < 1)
+      return fail(KDA_ERR_CONFIG, "state_pool_slots %lld", (long long)a->state_pool_slots);
+    if (a->state_slot_pitch != 0 && (a->state_slot_pitch < dense || a->state_slot_pitch % 8))
+      return fail(KDA_ERR_CONFIG, "state_slot_pitch %lld", (long long)a->state_slot_pitch);
+  }
   return KDA_OK;
+}
+
+// Elements of state_in / state_out the call may touch.
+size_t state_elems(const kda_prefill_args* a) {
+  const size_t dense = static_cast<size_t>(a->H) * KDA_HEAD_DIM * KDA_HEAD_DIM;
+  if (!a->ssm_state_indices) return static_cast<size_t>(a->N) * dense;
+  const size_t pitch = a->state_slot_pitch ? static_cast<size_t>(a->state_slot_pitch) : dense;
+  return (static_cast<size_t>(a->state_pool_slots) - 1) * pitch + dense;
 }
 
 int rows_per_wg(const kda_prefill_args* a, int num_cus) {
@@ -260,8 +276,9 @@ kda_status kda_prefill_check(const kda_prefill_args* a) {
   const size_t es = elem_size(a->io_dtype);
   const size_t tensor = static_cast<size_t>(tokens) * a->H * KDA_HEAD_DIM * es;
   const size_t beta_b = static_cast<size_t>(tokens) * a->H * es;
-  const size_t state_b = static_cast<size_t>(a->N) * a->H * KDA_HEAD_DIM * KDA_HEAD_DIM *
-                         elem_size(a->state_dtype);
+  const size_t state_b = state_elems(a) * elem_size(a->state_dtype);
+  if (a->ssm_state_indices && a->state_out && a->state_out != a->state_in)
+    return fail(KDA_ERR_ALIAS, "with a state pool, state_out must be NULL or state_in");
   const size_t need = workspace_need(a);
   if (need > 0) {
     if (!a->workspace) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -288,6 +305,8 @@ kda_status kda_prefill_check(const kda_prefill_args* a) {
       range_of(a->A_log, (a->flags & KDA_FLAG_GATE_IN_KERNEL) ? a->H * 4 : 0, "A_log"),
       range_of(a->dt_bias, (a->flags & KDA_FLAG_GATE_IN_KERNEL) ? a->H * 512 : 0, "dt_bias"),
       range_of(a->checkpoint_cu_starts, ckpt ? (a->N + 1) * 8 : 0, "checkpoint_cu_starts"),
+      range_of(a->ssm_state_indices, a->ssm_state_indices ? a->N * 4 : 0, "ssm_state_indices"),
+      range_of(a->seq_order, a->seq_order ? a->N * 4 : 0, "seq_order"),
   };
   const Range o = range_of(a->o, tensor, "o");
   const Range so = range_of(a->state_out, state_b, "state_out");
@@ -336,7 +355,7 @@ kda_status kda_prefill_plan(const kda_prefill_args* a, int32_t num_cus, kda_plan
     out->scan_c_workgroups = scan_c_workgroups(a, pl, rows);
     out->combine_workgroups = (a->H * a->N + 7) / 8 * 64;
   } else {
-    out->recurrence_workgroups = a->N * a->H * (KDA_HEAD_DIM / rows);
+    out->recurrence_workgroups = (a->N * a->H + 7) / 8 * 8 * (KDA_HEAD_DIM / rows);
   }
   out->scan_state_offset = pl.scan_s;
   out->scan_transition_offset = pl.scan_phi;
@@ -380,6 +399,14 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   p.seg_len = pl.seg_len;
   p.segs_per_seq = pl.segs_per_seq;
   p.seg_stride = pl.seg_stride;
+  if (a->ssm_state_indices) {
+    p.state_idx = a->ssm_state_indices;
+    p.pool_slots = a->state_pool_slots;
+    p.slot_pitch = a->state_slot_pitch ? a->state_slot_pitch
+                                        : a->H * KDA_HEAD_DIM * KDA_HEAD_DIM;
+    p.state_out = const_cast<void*>(a->state_in);  // the pool is updated in place
+  }
+  p.seq_order = a->seq_order;
   if (a->checkpoint_every > 0) {
     p.ckpt = a->state_checkpoints;
     p.ckpt_cu = a->checkpoint_cu_starts;
@@ -406,7 +433,8 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   if (e == hipSuccess && a->T > 0) e = kda::launch_prepare(p, io_bf16, stream);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
   if (pl.seg_len == 0) {
-    const int64_t wgs = a->N * a->H * (KDA_HEAD_DIM / rows);
+    // whole rounds of 8 (sequence, head) pairs over the XCDs, each with its row blocks
+    const int64_t wgs = (a->N * a->H + 7) / 8 * 8 * (KDA_HEAD_DIM / rows);
     if (e == hipSuccess) e = recurrence(wgs);
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[3], stream);
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[4], stream);

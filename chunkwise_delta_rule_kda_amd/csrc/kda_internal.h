@@ -60,6 +60,11 @@ struct Params {
   const int64_t* ckpt_cu;     // [N + 1] row offsets
   int64_t ckpt_every;         // chunks between checkpoints
   int64_t ckpt_rows;
+  // State pool (null: state n at [n][H][128][128]) and scheduling order.
+  const int32_t* state_idx;   // [N] slot of each sequence
+  int64_t pool_slots;
+  int64_t slot_pitch;         // elements between slots
+  const int32_t* seq_order;   // [N] or null
 };
 
 hipError_t launch_plan(const Params& p, hipStream_t stream);

@@ -189,6 +189,17 @@ __device__ __forceinline__ void seq_segments(const Params& p, int64_t n, int64_t
 __device__ bool segment_task(const Params& p, Task& t, int64_t h, int64_t n, int64_t seg,
                              int64_t first, int64_t nseg, int vr);
 
+// Element offset of state row r of (sequence n, head h) in state_in / state_out (a pool
+// slot with a state pool), or -1 when the sequence's slot id is out of range.
+__device__ __forceinline__ int64_t state_row(const Params& p, int64_t n, int64_t h, int r) {
+  if (p.state_idx) {
+    const int64_t slot = p.state_idx[n];
+    if (slot < 0 || slot >= p.pool_slots) return -1;
+    return slot * p.slot_pitch + (h * kD + r) * kD;
+  }
+  return ((n * p.H + h) * kD + r) * kD;
+}
+
 __device__ bool decode_task(const Params& p, int rows, Task& t) {
   const int64_t task = task_index();
   const int64_t H = p.H;
@@ -199,11 +210,20 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
   t.s_dst = nullptr;
   t.phi_dst = nullptr;
   if (p.mode == kModeSerial) {
-    const int blocks = kD / rows;
-    const int64_t sh = task / blocks;
-    const int blk = static_cast<int>(task - sh * blocks);
-    const int64_t n = sh / H;
-    if (n >= p.N) return false;
+    // Pairs (sequence slot s, head h), h fastest, are dispatched round-robin over the
+    // XCDs (workgroup b runs on XCD b % 8), so that every XCD gets a share of each
+    // sequence; the bpp row blocks of one pair share an XCD (and its L2): pair
+    // 8 (b / (8 bpp)) + b % 8, row block (b / 8) % bpp. Slot s runs sequence
+    // seq_order[s] when an order is given.
+    const int bpp = kD / rows;
+    const int64_t b = blockIdx.x;
+    const int64_t pair = (b / (8 * bpp)) * 8 + (b % 8);
+    const int blk = static_cast<int>((b / 8) % bpp);
+    if (pair >= p.N * H) return false;
+    const int64_t slot = pair / H;
+    const int64_t n = p.seq_order ? static_cast<int64_t>(p.seq_order[slot]) : slot;
+    if (n < 0 || n >= p.N) return false;
+    const int64_t sh = n * H + (pair - slot * H);
     int64_t start, end, chunk0, nch;
     seq_range(p, n, start, end, chunk0, nch);
     t.tok0 = start;
@@ -556,13 +576,13 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
   const int64_t nch = t.nch;
 
   // State rows v0 + m, keys 16 b + 4 grp + j: the 16x16x16 accumulator layout.
-  const int64_t srow = (t.sh * kD + v0 + m) * kD;
+  const int64_t srow = state_row(p, t.n, t.h, v0 + m);
   f32x4 st[8];
   bf16x8 sp[4];
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     const int key = 16 * b + 4 * grp;
-    if (t.start == kStartIn && p.state_in) {
+    if (t.start == kStartIn && p.state_in && srow >= 0) {
       st[b] = load4<BF16ST>(p.state_in, srow + key);
     } else if (t.start == kStartScan) {
       st[b] = load4<false>(t.s_src, state_frag(v0 >> 4, b, lane));
@@ -644,7 +664,7 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
     if (OUT) store_out(nch - 1, pend);
   }
 
-  if (t.final_state && p.state_out) {
+  if (t.final_state && p.state_out && srow >= 0) {
 #pragma unroll
     for (int b = 0; b < 8; ++b) store4<BF16ST>(p.state_out, srow + 16 * b + 4 * grp, st[b]);
   }

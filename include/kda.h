@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 #define KDA_HEAD_DIM 128 /* d_k = d_v = 128 */
 #define KDA_CHUNK 16     /* tokens per chunk */
 
@@ -59,13 +59,16 @@ typedef enum kda_status {
   KDA_ERR_DTYPE = 3,      /* io_dtype or state_dtype not a kda_dtype */
   KDA_ERR_FLAGS = 4,      /* unknown flag bit, or a flag's companion input missing */
   KDA_ERR_BOUND = 5,      /* lower_bound outside [-5, 0), or scale not finite */
-  KDA_ERR_ALIAS = 6,      /* an output overlaps an input (state_out == state_in is allowed) */
+  KDA_ERR_ALIAS = 6,      /* an output overlaps an input (state_out == state_in is allowed),
+                             or a state pool's state_out is neither NULL nor state_in */
   KDA_ERR_WORKSPACE = 7,  /* workspace NULL, too small or not 256-byte aligned */
   KDA_ERR_HIP = 8,        /* a HIP runtime call or kernel launch failed */
   KDA_ERR_CU_SEQLENS = 9, /* kda_debug_check_cu_seqlens found a contract violation */
   KDA_ERR_CONFIG = 10     /* rows_per_workgroup not 0, 16, 32 or 64, segment_chunks
                              above 2^24, checkpoint_every not a multiple of 16 (or
-                             negative), or checkpoint_rows negative */
+                             negative), checkpoint_rows negative, or a state pool
+                             with no slots, a pitch below H * 128 * 128 or not a
+                             multiple of 8, or no state_in */
 } kda_status;
 
 enum {
@@ -148,6 +151,26 @@ typedef struct kda_prefill_args {
   int64_t checkpoint_rows;
   void *state_checkpoints;
   const int64_t *checkpoint_cu_starts;
+
+  /* State pool (the "flashinfer.kda_prefill" page, section "State and graph
+     semantics"). ssm_state_indices: int32 [N] device, or NULL. When set, state_in is a
+     caller-owned pool of state_pool_slots slots of [H, 128, 128] (state_dtype), slot j
+     starting state_slot_pitch elements after slot j - 1 (0 = H * 128 * 128; otherwise at
+     least that and a multiple of 8), and sequence n starts from slot
+     ssm_state_indices[n] and writes its final state back to the same slot: state_in is
+     required and state_out must be NULL or equal to state_in. Slot ids must be unique
+     (caller contract, not checked); an id outside [0, state_pool_slots) makes that
+     sequence start from zero and write no state. Checkpoints still go to
+     state_checkpoints. */
+  const int32_t *ssm_state_indices;
+  int64_t state_pool_slots;
+  int64_t state_slot_pitch;
+
+  /* Scheduling order (the same page, section "Packed scheduling"): int32 [N] device, a
+     permutation of [0, N) (caller contract, not checked), or NULL for the natural
+     order. The serial form starts the sequences' workgroups in this order, so ordering
+     by decreasing length shortens the last partial wave. Results do not depend on it. */
+  const int32_t *seq_order;
 
   /* Optional timing hooks (host array of hipEvent_t handles, or NULL). When
      n_trace_events >= 3, the library records trace_events[0] before the first kernel,

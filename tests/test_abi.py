@@ -47,7 +47,7 @@ def test_record_size_matches_header():
 
 def test_abi_version_and_status_strings():
     lib = kda.load_library()
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     for code in range(11):
         assert kda.kda_status_string(code) and kda.kda_status_string(code) != "unknown status"
     assert kda.kda_status_string(99) == "unknown status"
@@ -155,6 +155,23 @@ def test_checkpoint_validation():
     assert status(fake(checkpoint_every=0, state_checkpoints=base + 2 * 256 * MB)) == 0
 
 
+def test_state_pool_and_order_validation():
+    base = 0x7F0000000000
+    dense = 2 * 128 * 128
+    pool = dict(ssm_state_indices=base + 12 * 256 * MB, state_pool_slots=5, state_out=None)
+    assert status(fake(**pool)) == 0
+    assert status(fake(**dict(pool, state_slot_pitch=dense + 64))) == 0
+    assert status(fake(**dict(pool, state_out=base + 5 * 256 * MB))) == 0   # == state_in
+    assert status(fake(**dict(pool, state_out=base + 7 * 256 * MB))) == 6   # elsewhere
+    assert status(fake(**dict(pool, state_in=None))) == 10
+    assert status(fake(**dict(pool, state_pool_slots=0))) == 10
+    assert status(fake(**dict(pool, state_slot_pitch=dense - 8))) == 10
+    assert status(fake(**dict(pool, state_slot_pitch=dense + 4))) == 10
+    assert status(fake(**dict(pool, ssm_state_indices=base + 6 * 256 * MB))) == 6  # == o
+    assert status(fake(seq_order=base + 13 * 256 * MB)) == 0
+    assert status(fake(seq_order=base + 6 * 256 * MB)) == 6                     # == o
+
+
 def test_misaligned_vector_pointer_rejected():
     assert status(fake(q=0x7F0000000000 + 8)) == 2
 
@@ -167,7 +184,8 @@ def test_plan_follows_the_slice_rule():
     p = kda.kda_prefill_plan(fake(H=96, T=8192), 256)
     assert p["rows_per_workgroup"] == 64 and p["recurrence_workgroups"] == 192
     assert p["prepare_workgroups"] == 512 * 96
-    assert kda.kda_prefill_plan(fake(H=6, rows_per_workgroup=64), 256)["recurrence_workgroups"] == 12
+    # serial grid: whole rounds of 8 (sequence, head) pairs, each with its row blocks
+    assert kda.kda_prefill_plan(fake(H=6, rows_per_workgroup=64), 256)["recurrence_workgroups"] == 16
     assert status(fake(rows_per_workgroup=128)) == 10
     assert status(fake(rows_per_workgroup=48)) == 10
 
