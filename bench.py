@@ -40,7 +40,8 @@ FLOP_PREP_PER_TOKEN_HEAD = 2 * 2 * C * D
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 
-KERNEL_SOURCES = ["kda_prepare.hip", "kda_recurrence.hip", "kda_device.h", "kda_internal.h"]
+KERNEL_SOURCES = ["kda_prepare.hip", "kda_recurrence.hip", "kda_decode.hip", "kda_device.h",
+                  "kda_internal.h"]
 
 
 def kernel_hash():
@@ -247,6 +248,17 @@ def summarize(x, r):
     tot_us = r["ms_per_step"] * 1e3
     alg_bytes = th * BYTES_PER_TOKEN_HEAD_BF16 + state_b
     alg_flop = th * (FLOP_REC_PER_TOKEN_HEAD + FLOP_PREP_PER_TOKEN_HEAD)
+    if x.T == 1 and x.cu_seqlens is None:
+        # Single-token form: one kernel (timed between the first two events), bound by
+        # the state read and write.
+        return dict(
+            us=round(tot_us, 2), tokens_per_s=round(x.tokens() / (tot_us * 1e-6), 1),
+            decode_kernel_us=round(prep_us, 2), state_bytes=state_b,
+            hbm_gbs=round(alg_bytes / (tot_us * 1e-6) / 1e9, 1),
+            hbm_frac=round(alg_bytes / (tot_us * 1e-6) / (PEAK_HBM_GBS * 1e9), 5),
+            event_marker_us=round(r["event_gap_ms"] * 1e3, 2),
+            per_call_us=r["per_call_us"],
+        )
     return dict(
         us=round(tot_us, 2), tokens_per_s=round(x.tokens() / (tot_us * 1e-6), 1),
         prepare_us=round(prep_us, 2), recurrence_us=round(rec_us, 2),
@@ -271,6 +283,7 @@ def main():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--extra-configs", default="2,3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter "
                          "calibration for rocprofv3 --pmc runs)")
@@ -347,6 +360,15 @@ def main():
                                                              2, device, hip))
         progress(f"config{c}: {per_config[f'config{c}']}")
         del xc
+        torch.cuda.empty_cache()
+    # Decode step (one token per sequence, the single-token kernel): B=256 sequences,
+    # H=32 heads, BF16 state drawn as config 2's; bound by the state's HBM traffic.
+    if not args.no_decode:
+        xd = kda_synth.config(2, B=256, T=1, H=32)
+        per_config["decode_B256_H32"] = summarize(
+            xd, time_config(xd, max(10, args.steps // 2), 3, device, hip))
+        progress(f"decode: {per_config['decode_B256_H32']}")
+        del xd
         torch.cuda.empty_cache()
     if "config1" in per_config and "config3" in per_config:
         per_config["head_scaling_t96_over_t6"] = round(

@@ -120,10 +120,11 @@ class kda_plan_info(ctypes.Structure):
         ("scan_c_workgroups", ctypes.c_int64),
         ("scan_state_offset", ctypes.c_size_t),
         ("scan_transition_offset", ctypes.c_size_t),
+        ("decode", ctypes.c_int32),
     ]
 
 
-ABI_VERSION = 4  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
+ABI_VERSION = 5  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
 
 
 def lib_path():

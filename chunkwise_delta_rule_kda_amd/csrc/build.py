@@ -13,7 +13,7 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libkda.so")
 
-SOURCES = ["kda_api.cpp", "kda_prepare.hip", "kda_recurrence.hip"]
+SOURCES = ["kda_api.cpp", "kda_prepare.hip", "kda_recurrence.hip", "kda_decode.hip"]
 HEADERS = ["kda_internal.h", "kda_device.h"]
 
 FLAGS = [

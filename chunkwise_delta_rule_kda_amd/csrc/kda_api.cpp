@@ -141,9 +141,16 @@ struct Plan {
   size_t total = 0;
 };
 
+// One token per sequence (fixed layout, no checkpoints): the single-token kernel, no
+// workspace.
+bool decode_form(const kda_prefill_args* a) {
+  return a->T == 1 && !a->cu_seqlens && a->checkpoint_every == 0;
+}
+
 Plan make_plan(const kda_prefill_args* a) {
   Plan pl;
   pl.max_chunks = max_chunks_of(a);
+  if (decode_form(a)) return pl;
   const int64_t per_seq = a->cu_seqlens ? (a->N > 0 ? pl.max_chunks / a->N : 0)
                                         : (a->T + kda::kC - 1) / kda::kC;
   int64_t L = 0;
@@ -359,6 +366,13 @@ kda_status kda_prefill_plan(const kda_prefill_args* a, int32_t num_cus, kda_plan
   }
   out->scan_state_offset = pl.scan_s;
   out->scan_transition_offset = pl.scan_phi;
+  if (decode_form(a)) {
+    out->decode = 1;
+    out->prepare_workgroups = 0;
+    out->recurrence_workgroups = a->N * a->H;
+    out->waves_per_workgroup = 4;
+    out->rows_per_workgroup = KDA_HEAD_DIM;
+  }
   return KDA_OK;
 }
 
@@ -428,6 +442,16 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   const bool ev5 = ev && a->n_trace_events >= 5;
 
   hipError_t e = hipSuccess;
+  if (decode_form(a)) {
+    if (ev) e = hipEventRecord(ev[0], stream);
+    if (e == hipSuccess) e = kda::launch_decode(p, io_bf16, st_bf16, stream);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
+    if (e == hipSuccess && ev5) e = hipEventRecord(ev[3], stream);
+    if (e == hipSuccess && ev5) e = hipEventRecord(ev[4], stream);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s", hipGetErrorString(e));
+    return KDA_OK;
+  }
   if (ev) e = hipEventRecord(ev[0], stream);
   if (e == hipSuccess && a->cu_seqlens) e = kda::launch_plan(p, stream);
   if (e == hipSuccess && a->T > 0) e = kda::launch_prepare(p, io_bf16, stream);

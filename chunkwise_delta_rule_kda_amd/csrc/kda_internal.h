@@ -73,5 +73,6 @@ int recurrence_loader_waves(int compute_waves);
 hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16,
                              bool state_bf16, hipStream_t stream);
 hipError_t launch_combine(const Params& p, hipStream_t stream);
+hipError_t launch_decode(const Params& p, bool io_bf16, bool state_bf16, hipStream_t stream);
 
 }  // namespace kda

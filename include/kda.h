@@ -13,6 +13,10 @@
  * kernel and a serial recurrence kernel whose 128 value rows are split across compute
  * units (section 3.1 of the same post: value rows never interact).
  *
+ * One token per sequence (T = 1 in the fixed layout, no checkpoints) is a decode step:
+ * a single-token kernel reads each state once, updates it in registers and writes it
+ * back; such a call needs no workspace (kda_prefill_workspace_bytes returns 0).
+ *
  * The calling contract follows the "flashinfer.kda_prefill" API page (sections
  * "Optimized Blackwell prefill subset", "SM120a prefill subset" and "State and graph
  * semantics"): contiguous [B, T, H, 128] q, k, v, g; [B, T, H] beta; one shared head
@@ -43,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 #define KDA_HEAD_DIM 128 /* d_k = d_v = 128 */
 #define KDA_CHUNK 16     /* tokens per chunk */
 
@@ -273,6 +277,7 @@ typedef struct kda_plan_info {
   int64_t scan_c_workgroups;       /* the re-run launch */
   size_t scan_state_offset;
   size_t scan_transition_offset;
+  int32_t decode;                  /* 1: one token per sequence, the single-token kernel */
 } kda_plan_info;
 kda_status kda_prefill_plan(const kda_prefill_args *a, int32_t num_cus, kda_plan_info *out);
 

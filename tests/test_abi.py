@@ -47,7 +47,7 @@ def test_record_size_matches_header():
 
 def test_abi_version_and_status_strings():
     lib = kda.load_library()
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
     for code in range(11):
         assert kda.kda_status_string(code) and kda.kda_status_string(code) != "unknown status"
     assert kda.kda_status_string(99) == "unknown status"
