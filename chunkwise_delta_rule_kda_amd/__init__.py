@@ -121,10 +121,12 @@ class kda_plan_info(ctypes.Structure):
         ("scan_state_offset", ctypes.c_size_t),
         ("scan_transition_offset", ctypes.c_size_t),
         ("decode", ctypes.c_int32),
+        ("scan_affine_output", ctypes.c_int32),
+        ("scan_output_offset", ctypes.c_size_t),
     ]
 
 
-ABI_VERSION = 5  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
+ABI_VERSION = 6  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
 
 
 def lib_path():

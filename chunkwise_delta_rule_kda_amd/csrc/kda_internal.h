@@ -18,8 +18,11 @@ constexpr int kOffMbAq = 12800;  // bf16 [L 64][Mb 4, A_qk 4]
 // Recurrence launch modes: one serial run per sequence, or the launches of the
 // segmented (time-parallel) form.
 constexpr int32_t kModeSerial = 0;
-constexpr int32_t kModeScanA = 1;  // segment 0 (true start) + Z_p, Phi_p of middle segments
+constexpr int32_t kModeScanA = 1;  // segment 0 (true start) + Z_p, Phi_p of later segments
 constexpr int32_t kModeScanC = 2;  // segments 1..P-1 again from their true start states
+
+// Chunks per workgroup of the scan-output launch (affine-output segmented form).
+constexpr int kScanOutChunks = 4;
 
 constexpr uint32_t kFlagL2 = 1u << 0;
 constexpr uint32_t kFlagGate = 1u << 1;
@@ -55,6 +58,12 @@ struct Params {
   int64_t* cu_segs;           // varlen: [N + 1] prefix of segments per sequence
   float* scan_s;              // FP32 [H][seg_stride][128][128]: S_p, Z_p
   unsigned short* scan_phi;   // BF16 [H][seg_stride][128 keys][128 rows]: Phi_p transposed
+  // Affine-output form: launch A also runs segment P-1 and writes O of the zero-start
+  // runs into o and O of the transition runs (Qt Phi^T per chunk) into scan_q; the
+  // combine's last step writes the final state; the scan-output launch then adds
+  // (Qt Phi^T) S_p^T to o instead of rerunning the segments.
+  int32_t affine_out;
+  void* scan_q;               // IO dtype [H][max_chunks][kb 4][lane 64][8]
   // State checkpoints (ckpt_every chunks apart; 0 = none).
   void* ckpt;                 // [ckpt_rows][H][128][128] of the state dtype
   const int64_t* ckpt_cu;     // [N + 1] row offsets
@@ -72,7 +81,9 @@ hipError_t launch_prepare(const Params& p, bool io_bf16, hipStream_t stream);
 int recurrence_loader_waves(int compute_waves);
 hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16,
                              bool state_bf16, hipStream_t stream);
-hipError_t launch_combine(const Params& p, hipStream_t stream);
+hipError_t launch_combine(const Params& p, bool state_bf16, hipStream_t stream);
+hipError_t launch_scan_output(const Params& p, int64_t workgroups, bool io_bf16,
+                              hipStream_t stream);
 hipError_t launch_decode(const Params& p, bool io_bf16, bool state_bf16, hipStream_t stream);
 
 }  // namespace kda

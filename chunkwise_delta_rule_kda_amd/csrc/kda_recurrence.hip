@@ -239,13 +239,15 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
     return true;
   }
   // Fixed layout: only the active row blocks are launched. Per sequence, launch A has
-  // the b0 = 128 / rows value blocks of segment 0, then for segments 1 .. P-2 the b0
-  // value (Z) and b0 transition (Phi) blocks; launch C the b0 value blocks of segments
-  // 1 .. P-1. Varlen: a bound of seg_stride slots x p.blocks per head, decoded below.
+  // the b0 = 128 / rows value blocks of segment 0, then for segments 1 .. P-2 (1 .. P-1
+  // in the affine-output form) the b0 value (Z) and b0 transition (Phi) blocks; launch
+  // C the b0 value blocks of segments 1 .. P-1. Varlen: a bound of seg_stride slots x
+  // p.blocks per head, decoded below.
   if (!p.cu_seqlens) {
     const int b0 = kD / rows;
     const int64_t P = p.segs_per_seq;
-    const int64_t per_seq = p.mode == kModeScanA ? (P >= 2 ? b0 + 2 * b0 * (P - 2) : b0)
+    const int64_t mid = p.affine_out ? P - 1 : P - 2;  // segments with Z and Phi runs
+    const int64_t per_seq = p.mode == kModeScanA ? (P >= 2 ? b0 + 2 * b0 * mid : b0)
                                                  : (P - 1) * b0;
     if (per_seq <= 0) return false;
     const int64_t per_head = p.N * per_seq;
@@ -294,7 +296,7 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
   const int64_t seg = gsg - first;
   const int vr = blk * rows;
   if (p.mode == kModeScanA) {
-    if (nseg >= 2 && seg == nseg - 1) return false;  // last segment: only in launch C
+    if (!p.affine_out && nseg >= 2 && seg == nseg - 1) return false;  // only in launch C
     if (vr >= kD && seg == 0) return false;           // no transition for segment 0
   } else if (seg == 0) {
     return false;                                     // segment 0: only in launch A
@@ -326,14 +328,19 @@ __device__ bool segment_task(const Params& p, Task& t, int64_t h, int64_t n, int
     if (vr < kD) {
       t.vwg = vr;
       t.start = seg == 0 ? kStartIn : kStartZero;
-      t.out = seg == 0;
+      t.out = seg == 0 || p.affine_out;  // affine-output form: O of the zero start
       t.final_state = nseg == 1;
-      if (nseg >= 2) t.s_dst = p.scan_s + (slot + 1) * (kD * kD);  // S_1, or Z_seg
+      if (nseg >= 2) {
+        // S_1 (segment 0) or Z_seg into slot seg + 1; the last segment's Z (affine-output
+        // form only) into the sequence's first slot, which never holds a start state.
+        const int64_t zs = seg == nseg - 1 ? h * p.seg_stride + first : slot + 1;
+        t.s_dst = p.scan_s + zs * (kD * kD);
+      }
     } else {
       t.vwg = vr - kD;
       t.start = kStartIdentity;
       t.vzero = true;
-      t.out = false;
+      t.out = p.affine_out;  // affine-output form: Qt Phi^T per chunk into scan_q
       t.final_state = false;
       t.phi_dst = p.scan_phi + slot * (kD * kD);
     }
@@ -608,10 +615,22 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
     // The O of chunk c is stored in iteration c + 1, after that iteration's MFMA work
     // has been issued, so that its wait for chunk c's last products is hidden.
     f32x4 pend = {0.f, 0.f, 0.f, 0.f};
-    const int64_t obase = t.tok0 * vstride + t.h * kD + v0;
+    // O[token m][rows v0 + 4 grp + j] goes to o. A transition run (affine-output form)
+    // writes Qt Phi^T instead: its rows v0 + 4 grp + j are the keys of that product,
+    // stored per chunk in the Qt operand layout [kb 4][lane 64][e 8] of scan_q (key
+    // 32 kb + 16 (e / 4) + 4 grp + e % 4 of token m in lane 16 grp + m), which puts
+    // this lane's four values in its own lane, block v0 / 32, elements 4 (v0 / 16 % 2) + j.
+    void* obuf = p.o;
+    int64_t ooff = (t.tok0 + m) * vstride + t.h * kD + v0 + 4 * grp;
+    int64_t ostep = kC * vstride;
+    if (t.vzero) {
+      obuf = p.scan_q;
+      ooff = (t.h * p.max_chunks + t.rec_chunk) * (4 * 64 * 8) + ((v0 >> 5) * 64 + lane) * 8 +
+             ((v0 >> 4) & 1) * 4;
+      ostep = 4 * 64 * 8;
+    }
     auto store_out = [&](int64_t c, f32x4 val) {
-      if (m < t.tok_end - (t.tok0 + c * kC))
-        store4<BF16IO>(p.o, obase + (c * kC + m) * vstride + 4 * grp, val);
+      if (m < t.tok_end - (t.tok0 + c * kC)) store4<BF16IO>(obuf, ooff + c * ostep, val);
     };
     TailIn tail;
     read_tail<OUT>(tail, ring, lane);
@@ -716,7 +735,8 @@ __global__ __launch_bounds__(block_threads(W), 2) void kda_recurrence_kernel(Par
 }
 
 // Launch B of the segmented form: S_{p+1} = S_p Phi_p + Z_p, p = 1 .. P-2, for 16 value
-// rows of one (sequence, head) per workgroup. In the transposed form S^T_{p+1} =
+// rows of one (sequence, head) per workgroup; in the affine-output form also p = P-1,
+// whose result is the final state. In the transposed form S^T_{p+1} =
 // Phi_p^T S_p^T + Z_p^T; wave w computes output key blocks 2 w and 2 w + 1 (eight
 // 16x16x32 products). Phi_p^T, stored as A-operand fragments by launch A, is the A
 // operand: one 1 KB contiguous load per wave and product, and a wave's slice of Phi
@@ -732,6 +752,7 @@ struct CombineIn {
   f32x4 z[2];     // Z rows v0 + m, keys 16 (2 w + i) + 4 grp + j
 };
 
+template <bool BF16ST>
 __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) unsigned char xch_[2 * 4 * 64 * 16];
   lds_u8* xbase = (lds_u8*)(xch_);  // address-space cast
@@ -746,17 +767,18 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   if (h >= p.H) return;
   int64_t first, nseg;
   seq_segments(p, n, first, nseg);
-  if (nseg < 3 || first < 0 || first + nseg > p.seg_stride) return;  // nothing to combine
+  const int64_t last = p.affine_out ? nseg - 1 : nseg - 2;  // steps s = 1 .. last
+  if (last < 1 || first < 0 || first + nseg > p.seg_stride) return;  // nothing to combine
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int64_t slot0 = h * p.seg_stride + first;
   float* sbase = p.scan_s + slot0 * (kD * kD);
   const unsigned char* pbase = reinterpret_cast<const unsigned char*>(p.scan_phi + slot0 * (kD * kD));
-  const int64_t last = nseg - 2;  // steps s = 1 .. last
   // This lane's fragment offsets: output key blocks b = 2 wave + i of row block rb.
   const int64_t koff0 = state_frag(rb, 2 * wave, lane);
   const int64_t koff1 = state_frag(rb, 2 * wave + 1, lane);
   const int aoff = (2 * wave * 4 * 64 + lane) * 16;  // bytes: block 2 wave, group 0
+  const int64_t srow = state_row(p, n, h, 16 * rb + (lane & 15));  // final state row
 
   auto fetch = [&](CombineIn& x, int64_t s) {
     s = s < last ? s : last;  // past the last step: re-read it (in bounds, unused)
@@ -766,7 +788,8 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         x.a[i][kk] = *reinterpret_cast<const u32x4*>(ph + (i * 4 + kk) * 1024);
-    const float* z = sbase + (s + 1) * (kD * kD);  // Z_s lives in slot s + 1
+    // Z_s lives in slot s + 1; the last segment's (affine-output form) in slot 0.
+    const float* z = sbase + (s + 1 < nseg ? s + 1 : 0) * (kD * kD);
     x.z[0] = load4<false>(z, koff0);
     x.z[1] = load4<false>(z, koff1);
   };
@@ -806,9 +829,14 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
       st[i] = acc + in[set].z[i];
     }
     *xch((s + 1) & 1, wave) = pack8(st[0], st[1]);
-    float* out = sbase + (s + 1) * (kD * kD);  // S_{s+1} replaces Z_s
-    store4<false>(out, koff0, st[0]);
-    store4<false>(out, koff1, st[1]);
+    if (s + 1 < nseg) {
+      float* out = sbase + (s + 1) * (kD * kD);  // S_{s+1} replaces Z_s
+      store4<false>(out, koff0, st[0]);
+      store4<false>(out, koff1, st[1]);
+    } else if (p.state_out && srow >= 0) {  // S_P: the final state
+      store4<BF16ST>(p.state_out, srow + 16 * (2 * wave) + 4 * (lane >> 4), st[0]);
+      store4<BF16ST>(p.state_out, srow + 16 * (2 * wave + 1) + 4 * (lane >> 4), st[1]);
+    }
     fetch(in[set], s + kCombineDepth);
     lds_barrier();
   };
@@ -821,6 +849,130 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   }
   if (s <= last) step(IntC<0>{}, s);
   if (s + 1 <= last) step(IntC<1>{}, s + 1);
+}
+
+// Scan-output launch of the affine-output form. Over segment p the state is affine in
+// its start state: S_c = S_p Phi_{p,c} + Z_{p,c}, so the output of chunk c is
+// O_c = O^Z_c + (Qt_c Phi_{p,c}^T) S_p^T, where O^Z_c is the output of the zero-start
+// run and Qt_c Phi_{p,c}^T the output of the transition run, both written by launch A
+// (into o and scan_q). Every chunk of segments 1 .. P-1 is then independent: this
+// launch adds the second term to o, kScanOutChunks chunks of one segment per
+// workgroup, wave w for values 32 w .. 32 w + 31 (row blocks 2 w, 2 w + 1). Per chunk a
+// wave runs eight 16x16x32 products with S_p (packed once) as the A operand and the
+// chunk's Qt Phi^T fragments (four contiguous 1 KB pieces) as the B operand. The
+// launch moves little data (the o term is read and written once, Qt Phi^T read once),
+// so it is bound by load latency: small workgroups, all resident in one round.
+struct ScanOutIn {
+  bf16x8 q[4];  // Qt Phi^T fragments of the chunk
+  f32x4 oz[2];  // O^Z[token m][values 16 rb + 4 grp + j], rb = 2 w + i
+};
+
+template <bool BF16IO>
+__device__ __forceinline__ bf16x8 load_frag(const void* base, int64_t idx) {
+  if constexpr (BF16IO) {
+    return *reinterpret_cast<const bf16x8*>(static_cast<const unsigned short*>(base) + idx);
+  } else {
+    const f32x4* f = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+    return pack8(f[0], f[1]);
+  }
+}
+
+template <bool BF16IO>
+__global__ __launch_bounds__(256, BF16IO ? 3 : 2) void kda_scan_output_kernel(Params p) {
+  const int64_t groups = (p.seg_len + kScanOutChunks - 1) / kScanOutChunks;
+  const int64_t task = task_index();  // consecutive tasks (one segment) share an XCD
+  const int64_t H = p.H;
+  int64_t h, n, seg, gi, first, nseg;
+  if (!p.cu_seqlens) {
+    const int64_t P = p.segs_per_seq;
+    const int64_t per_seq = (P - 1) * groups;
+    const int64_t per_head = p.N * per_seq;
+    if (per_head <= 0) return;
+    h = task / per_head;
+    if (h >= H) return;
+    int64_t rem = task - h * per_head;
+    n = rem / per_seq;
+    rem -= n * per_seq;
+    seg = 1 + rem / groups;
+    gi = rem - (seg - 1) * groups;
+    first = n * P;
+    nseg = P;
+  } else {
+    const int64_t per_head = p.seg_stride * groups;
+    h = task / per_head;
+    if (h >= H) return;
+    const int64_t rem = task - h * per_head;
+    const int64_t gsg = rem / groups;
+    gi = rem - gsg * groups;
+    if (gsg >= p.cu_segs[p.N]) return;
+    int64_t lo = 0, hi = p.N - 1;  // largest n with cu_segs[n] <= gsg
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (p.cu_segs[mid] <= gsg) lo = mid;
+      else hi = mid - 1;
+    }
+    n = lo;
+    seq_segments(p, n, first, nseg);
+    seg = gsg - first;
+  }
+  if (seg < 1 || seg >= nseg || first < 0 || first + nseg > p.seg_stride) return;
+  int64_t start, end, chunk0, nch;
+  seq_range(p, n, start, end, chunk0, nch);
+  const int64_t c0 = seg * p.seg_len + gi * kScanOutChunks;
+  const int64_t c1 = min(min(c0 + kScanOutChunks, (seg + 1) * p.seg_len), nch);
+  if (c0 >= c1) return;
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int m = lane & 15;
+  const int grp = lane >> 4;
+  // S_p rows 16 rb + m, packed as the recurrence packs its state (keys in the 16x16x32
+  // operand order).
+  const float* sp_src = p.scan_s + (h * p.seg_stride + first + seg) * (kD * kD);
+  f32x4 sp_f[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) sp_f[i][b] = load4<false>(sp_src, state_frag(2 * wave + i, b, lane));
+
+  const int64_t vstride = H * kD;
+  const int64_t qbase = (h * p.max_chunks + chunk0) * (4 * 64 * 8) + lane * 8;
+  const int64_t obase = (start + m) * vstride + h * kD + 32 * wave + 4 * grp;
+  // Every load of the workgroup is issued before the first product: the latency of one
+  // round trip, not one per chunk, sets the time. Chunks past c1 re-read chunk c1 - 1
+  // (in bounds, never stored).
+  ScanOutIn in[kScanOutChunks];
+#pragma unroll
+  for (int j = 0; j < kScanOutChunks; ++j) {
+    const int64_t c = min(c0 + j, c1 - 1);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      in[j].q[kb] = load_frag<BF16IO>(p.scan_q, qbase + c * (4 * 64 * 8) + kb * 64 * 8);
+    if (m < end - (start + c * kC)) {
+      in[j].oz[0] = load4<BF16IO>(p.o, obase + c * kC * vstride);
+      in[j].oz[1] = load4<BF16IO>(p.o, obase + c * kC * vstride + 16);
+    }
+  }
+  bf16x8 sa[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      sa[i][kb] = pack8(sp_f[i][2 * kb], sp_f[i][2 * kb + 1]);
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kScanOutChunks; ++j) {
+    const int64_t c = c0 + j;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      f32x4 acc = mfma32(sa[i][0], in[j].q[0], zero);
+      acc = mfma32(sa[i][1], in[j].q[1], acc);
+      acc = mfma32(sa[i][2], in[j].q[2], acc);
+      acc = mfma32(sa[i][3], in[j].q[3], acc);
+      if (c < c1 && m < end - (start + c * kC))
+        store4<BF16IO>(p.o, obase + c * kC * vstride + 16 * i, acc + in[j].oz[i]);
+    }
+  }
 }
 
 template <bool BF16IO, bool BF16ST, bool CK>
@@ -868,12 +1020,24 @@ hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16, 
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Params& p, hipStream_t stream) {
+hipError_t launch_scan_output(const Params& p, int64_t workgroups, bool io_bf16,
+                              hipStream_t stream) {
+  if (workgroups <= 0) return hipSuccess;
+  workgroups = (workgroups + 7) / 8 * 8;  // whole XCD rounds (see task_index)
+  if (workgroups > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(workgroups));
+  if (io_bf16) hipLaunchKernelGGL(kda_scan_output_kernel<true>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(kda_scan_output_kernel<false>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Params& p, bool state_bf16, hipStream_t stream) {
   const int64_t wgs = (p.H * p.N + 7) / 8 * 64;  // 8 row blocks per pair, pairs by XCD
   if (wgs <= 0) return hipSuccess;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kda_combine_kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream,
-                     p);
+  const dim3 grid(static_cast<unsigned>(wgs));
+  if (state_bf16) hipLaunchKernelGGL(kda_combine_kernel<true>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(kda_combine_kernel<false>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

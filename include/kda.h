@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 #define KDA_HEAD_DIM 128 /* d_k = d_v = 128 */
 #define KDA_CHUNK 16     /* tokens per chunk */
 
@@ -127,11 +127,16 @@ typedef struct kda_prefill_args {
 
   /* Time segments of the recurrence. The chunk-to-chunk carry is affine in the state,
      so a sequence can be cut into segments of this many chunks that run in parallel:
-     each middle segment's transition (128 x 128) and zero-start end state are computed
-     first, the segment start states are then combined serially (one 128x128x128
-     product per segment), and every segment is re-run from its true start to produce
-     o. It trades about three times the recurrence work for a critical path of about
-     two segments, which pays off when few (sequence, head) pairs leave compute units
+     each later segment's transition Phi (128 x 128) and zero-start run are computed
+     first, and the segment start states are then combined serially (one 128x128x128
+     product per segment). Without checkpoints (the affine-output form) the first pass
+     also writes each later segment's zero-start output into o and the output of its
+     transition run (Qt Phi^T per chunk) into the workspace, the combine's last step
+     writes the final state, and a parallel pass adds (Qt Phi^T) S_p^T to o: a critical
+     path of about one segment plus the combine. With checkpoints every later segment
+     is instead re-run from its true start (the states inside it are needed): about two
+     segments. Either way about twice or three times the recurrence work buys the
+     shorter path, which pays off when few (sequence, head) pairs leave compute units
      idle. 0 = automatic (segments only when N * H <= 32, sized so the first pass has
      about one workgroup per compute unit of a 256-CU device); negative = never (one
      serial run per sequence); positive = this many chunks per segment. Results differ
@@ -206,10 +211,14 @@ typedef struct kda_prefill_args {
  *                                 MFMA fragments [row block 8][key block 8][lane 64][4]
  *                                 with lane 16 g + m holding S[16 rb + m][16 b + 4 g + j].
  *   scan_transition_offset        segmented form only: BF16 [H][S] slots of 128 x 128,
- *                                 each middle segment's transition Phi, as fragments
+ *                                 each later segment's transition Phi, as fragments
  *                                 [key block 8][key group 4][lane 64][8] with lane
  *                                 16 g + m holding Phi[k][16 b + m] for the keys
  *                                 k = 32 kk + 16 (e / 4) + 4 g + e % 4.
+ *   scan_output_offset            affine-output form only: [H][max_chunks] pieces of
+ *                                 2048 elements of the io dtype, Qt Phi^T of each
+ *                                 chunk of a later segment (Phi from the segment start
+ *                                 to the chunk start), in the record's Qt layout.
  * KDA_WS_HEADER = round_up((N + 1) * 16, 256) for varlen, 0 for the fixed layout.
  *
  * A record holds, for the chunk's 16 tokens (pad tokens of a short last chunk behave as
@@ -274,10 +283,13 @@ typedef struct kda_plan_info {
   int64_t segment_chunks;          /* 0: serial form */
   int64_t segments_per_head_bound; /* scan slots per head */
   int64_t combine_workgroups;
-  int64_t scan_c_workgroups;       /* the re-run launch */
+  int64_t scan_c_workgroups;       /* the re-run launch, or the scan-output launch of the
+                                      affine-output form */
   size_t scan_state_offset;
   size_t scan_transition_offset;
   int32_t decode;                  /* 1: one token per sequence, the single-token kernel */
+  int32_t scan_affine_output;      /* 1: the affine-output segmented form */
+  size_t scan_output_offset;
 } kda_plan_info;
 kda_status kda_prefill_plan(const kda_prefill_args *a, int32_t num_cus, kda_plan_info *out);
 

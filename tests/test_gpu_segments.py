@@ -1,10 +1,13 @@
 """The segmented (time-parallel) form of the recurrence vs the FP64 oracle.
 
 The chunk carry is affine in the state, so a sequence cut into segments is evaluated as:
-the first segment from the true initial state; each middle segment's zero-start end
-state Z_p and transition Phi_p; the serial combine S_{p+1} = S_p Phi_p + Z_p; and every
-later segment re-run from S_p. These tests force segment lengths from one chunk upward
-so that every part runs (no combine with two segments, one combine step with three,
+the first segment from the true initial state; each later segment's zero-start run
+(its end state Z_p and its output O^Z) and transition run (Phi_p, and Qt Phi^T per
+chunk); the serial combine S_{p+1} = S_p Phi_p + Z_p, whose last step gives the final
+state; and a parallel pass adding (Qt Phi^T) S_p^T to each later chunk's output (the
+affine-output form, taken when no checkpoints are asked for; the re-run form that
+checkpoints need is covered by the checkpoint tests). These tests force segment lengths
+from one chunk upward so that every part runs (a single combine step with two segments,
 many with one-chunk segments), on inputs whose decay is weak enough that the carry
 across segments decides the result. Bound: max|err| / max|ref| <= 2e-2.
 """
