@@ -137,7 +137,8 @@ def time_config(x, steps, warmup, device, hip, **extra):
     """Three passes over `steps` calls each:
     1. untimed-inside: the calls back to back between two events (the step time);
     2. traced: the library records five events per call between its launches, giving
-       the prepare / first recurrence launch / combine / re-run durations;
+       the prepare / first recurrence launch / combine / last launch (scan output)
+       durations;
     3. calibration: two events recorded back to back, `steps` times. Each traced phase
        spans exactly one event record (its start marker), whose stream time is this
        gap; it is subtracted from every phase."""
@@ -199,7 +200,7 @@ def time_config(x, steps, warmup, device, hip, **extra):
                               p90=round(us[min(steps - 1, int(0.9 * steps))], 2))
     del flush
     fix = lambda xs: [max(0.0, v - gap) for v in xs]
-    # The serial form has no combine or re-run launch: those phases hold only markers.
+    # The serial form has no combine or third launch: those phases hold only markers.
     serial = statistics.median(comb) <= 1.5 * gap and statistics.median(rec_c) <= 1.5 * gap
     return dict(ms_per_step=total_ms / steps, wall_s=t_wall, prep_ms=fix(prep),
                 rec_ms=[max(0.0, v - 3 * gap) for v in rec],  # ev 1 -> 2 spans three records
@@ -269,7 +270,7 @@ def summarize(x, r):
         recurrence_phases_us=dict(
             first=round(statistics.mean(r["rec_a_ms"]) * 1e3, 2),
             combine=round(statistics.mean(r["combine_ms"]) * 1e3, 2),
-            rerun=round(statistics.mean(r["rec_c_ms"]) * 1e3, 2)),
+            scan_output=round(statistics.mean(r["rec_c_ms"]) * 1e3, 2)),
         event_marker_us=round(r["event_gap_ms"] * 1e3, 2),
         per_call_us=r["per_call_us"],
     )
@@ -333,12 +334,14 @@ def main():
     main_s = summarize(x, r)
     progress(f"config{args.config}: {main_s}")
 
-    # Dominant kernel: the recurrence kernel (the serial chain), one launch per call in the
-    # serial form, two (the first segments and the re-run) in the segmented form. Roofline
-    # on its algorithmic MFMA work (the method's contractions, split evenly over the
-    # launches) per average launch duration.
-    launches = 1 if r["serial"] else 2
-    kern_us = (statistics.mean(r["rec_a_ms"]) + statistics.mean(r["rec_c_ms"])) * 1e3
+    # Dominant kernel: the recurrence kernel (the serial chain). It runs once per call in
+    # the serial form and in the affine-output segmented form (the first launch: segment
+    # 0 and the zero-start and transition runs of the later segments; the combine and the
+    # scan-output pass are other kernels), which is the form a call without checkpoints
+    # takes. Roofline on the path's algorithmic MFMA work of the recurrence (all token-
+    # heads pass through this launch) per launch duration.
+    launches = 1
+    kern_us = statistics.mean(r["rec_a_ms"]) * 1e3
     avg_launch_us = kern_us / launches
     th = x.tokens() * x.H
     rec_flop = th * FLOP_REC_PER_TOKEN_HEAD
