@@ -811,8 +811,8 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   *xch(1, wave) = pack8(st[0], st[1]);  // S_1, read by step 1
   lds_barrier();
 
-  // Step s: S_{s+1} = S_s Phi_s + Z_s with operands in set (s - 1) % 3; the set is then
-  // refilled with step s + 3. Whole groups of three steps are unrolled without
+  // Step s: S_{s+1} = S_s Phi_s + Z_s with operands in set (s - 1) % depth; the set is
+  // then refilled with step s + depth. Whole groups of depth steps are unrolled without
   // conditions so that the compiler's wait before each step is for its own set only.
   auto step = [&](auto set_c, int64_t s) {
     constexpr int set = decltype(set_c)::value;
@@ -842,13 +842,11 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   };
   int64_t s = 1;
 #pragma unroll 1
-  for (; s + 2 <= last; s += 3) {
-    step(IntC<0>{}, s);
-    step(IntC<1>{}, s + 1);
-    step(IntC<2>{}, s + 2);
-  }
-  if (s <= last) step(IntC<0>{}, s);
-  if (s + 1 <= last) step(IntC<1>{}, s + 1);
+  for (; s + kCombineDepth - 1 <= last; s += kCombineDepth)
+    unroll<kCombineDepth>([&](auto d) { step(d, s + decltype(d)::value); });
+  unroll<kCombineDepth - 1>([&](auto d) {
+    if (s + decltype(d)::value <= last) step(d, s + decltype(d)::value);
+  });
 }
 
 // Scan-output launch of the affine-output form. Over segment p the state is affine in

@@ -217,6 +217,25 @@ def test_linearity_in_values_and_initial_state():
     assert rel_err(s3, a * s1 + b * s2) < 1e-12
 
 
+def test_outputs_are_affine_in_the_start_state():
+    # With V = 0 and the identity as start state (Dk x Dk), the recurrence carries the
+    # product Phi_t of the token transitions, and its output at token t is s Phi_t q_t.
+    # For any start state S0: o_t(S0) = o_t(0) + S0 (s Phi_t q_t) and
+    # S_T(S0) = S0 Phi_T + S_T(0). This is the decomposition the GPU's segmented form
+    # evaluates (zero-start run, transition run, then the start state applied to both).
+    rng = np.random.default_rng(18)
+    Dk, Dv, T = 8, 6, 23
+    q, k, v, g, beta, S0 = rand_inputs(rng, 1, T, 2, Dk, Dv=Dv, g_lo=-0.3)
+    o, S = kda_recurrence_fp64(q, k, v, g, beta, S0, scale=0.7)
+    oz, Sz = kda_recurrence_fp64(q, k, v, g, beta, None, scale=0.7)
+    eye = np.broadcast_to(np.eye(Dk), (1, 2, Dk, Dk)).copy()
+    ophi, Phi = kda_recurrence_fp64(q, k, np.zeros((1, T, 2, Dk)), g, beta, eye, scale=0.7)
+    assert rel_err(o, oz + np.einsum("bhvr,bthr->bthv", S0, ophi)) < 1e-12
+    assert rel_err(S, Sz + np.einsum("bhvr,bhrk->bhvk", S0, Phi)) < 1e-12
+    # The carry matters here: the start state changes the outputs at the last token.
+    assert rel_err(o[:, -1], oz[:, -1]) > 1e-2
+
+
 def test_channel_permutation_equivariance():
     rng = np.random.default_rng(17)
     q, k, v, g, beta, S0 = rand_inputs(rng, 1, 19, 2, 8)
