@@ -243,18 +243,21 @@ def progress(msg):
 
 def summarize(x, r):
     th = x.tokens() * x.H
-    state_b = (2 if x.state0 is not None else 1) * x.N * x.H * D * D * 2
+    # Element sizes: FP32 configurations move twice the bytes of the BF16 figures.
+    es = 2 if x.dtype == "bf16" else 4
+    ess = 2 if x.state_dtype == "bf16" else 4
+    state_b = (2 if x.state0 is not None else 1) * x.N * x.H * D * D * ess
     prep_us = statistics.mean(r["prep_ms"]) * 1e3
     rec_us = statistics.mean(r["rec_ms"]) * 1e3
     tot_us = r["ms_per_step"] * 1e3
-    alg_bytes = th * BYTES_PER_TOKEN_HEAD_BF16 + state_b
+    alg_bytes = th * BYTES_PER_TOKEN_HEAD_BF16 * es // 2 + state_b
     alg_flop = th * (FLOP_REC_PER_TOKEN_HEAD + FLOP_PREP_PER_TOKEN_HEAD)
     if x.T == 1 and x.cu_seqlens is None:
         # Single-token form: one kernel (timed between the first two events), bound by
         # the state read and write.
         return dict(
             us=round(tot_us, 2), tokens_per_s=round(x.tokens() / (tot_us * 1e-6), 1),
-            decode_kernel_us=round(prep_us, 2), state_bytes=state_b,
+            decode_kernel_us=round(prep_us, 2), state_bytes=state_b, alg_bytes=alg_bytes,
             hbm_gbs=round(alg_bytes / (tot_us * 1e-6) / 1e9, 1),
             hbm_frac=round(alg_bytes / (tot_us * 1e-6) / (PEAK_HBM_GBS * 1e9), 5),
             event_marker_us=round(r["event_gap_ms"] * 1e3, 2),
@@ -265,6 +268,7 @@ def summarize(x, r):
         prepare_us=round(prep_us, 2), recurrence_us=round(rec_us, 2),
         hbm_frac=round(alg_bytes / (tot_us * 1e-6) / (PEAK_HBM_GBS * 1e9), 5),
         mfma_frac=round(alg_flop / (tot_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 5),
+        alg_bytes=alg_bytes, alg_flop=alg_flop,
         link_ns=round(rec_us * 1e3 / max(1, (x.T + C - 1) // C), 1) if x.cu_seqlens is None
         else None,
         recurrence_phases_us=dict(
@@ -282,7 +286,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1)
-    ap.add_argument("--extra-configs", default="2,3")
+    ap.add_argument("--extra-configs", default="0,2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -326,6 +330,22 @@ def main():
     s1.record()
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * (1 << 30) / (s0.elapsed_time(s1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    # Achievable dense BF16 MFMA rate on this machine: a plain 8192^3 product by the vendor
+    # library (contiguous operands), best of five after warm-up.
+    a = torch.randn(8192, 8192, device=device).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=device).to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        torch.mm(a, b)
+    gemm = []
+    for _ in range(5):
+        s0.record()
+        torch.mm(a, b)
+        s1.record()
+        torch.cuda.synchronize()
+        gemm.append(2 * 8192 ** 3 / (s0.elapsed_time(s1) * 1e-3) / 1e12)
+    gemm_tflops = max(gemm)
     del a, b
     torch.cuda.empty_cache()
 
@@ -373,6 +393,13 @@ def main():
         progress(f"decode: {per_config['decode_B256_H32']}")
         del xd
         torch.cuda.empty_cache()
+    # Fractions against the rates measured on this machine as well as the published peaks.
+    for v in per_config.values():
+        if isinstance(v, dict) and "alg_bytes" in v:
+            t = v["us"] * 1e-6
+            v["hbm_frac_of_measured_copy"] = round(v["alg_bytes"] / t / (copy_gbs * 1e9), 5)
+            if "alg_flop" in v:
+                v["mfma_frac_of_measured_gemm"] = round(v["alg_flop"] / t / (gemm_tflops * 1e12), 5)
     if "config1" in per_config and "config3" in per_config:
         per_config["head_scaling_t96_over_t6"] = round(
             per_config["config3"]["us"] / per_config["config1"]["us"], 3)
@@ -399,6 +426,7 @@ def main():
                    "seq_len": x.T, "heads": x.H, "parallelism": "single-gpu"},
         "roofline": roofline,
         "hbm_copy_measured_gbs": round(copy_gbs, 1),
+        "mfma_bf16_gemm_measured_tflops": round(gemm_tflops, 1),
         "cpu_baseline": cpu,
         "per_config": per_config,
         "kernel_source_hash": kernel_hash(),
