@@ -133,6 +133,36 @@ def make_call(x, device, **extra):
     return call, (o, st)
 
 
+def time_graph(x, steps, warmup, device):
+    """Microseconds per call when one kda_prefill call is captured in a HIP graph and the
+    graph is replayed back to back (the capture semantics are covered by the graph tests)."""
+    import torch
+
+    call, _ = make_call(x, device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(steps):
+        graph.replay()
+    s1.record()
+    torch.cuda.synchronize()
+    us = s0.elapsed_time(s1) / steps * 1e3
+    del graph
+    return round(us, 2)
+
+
 def time_config(x, steps, warmup, device, hip, **extra):
     """Three passes over `steps` calls each:
     1. untimed-inside: the calls back to back between two events (the step time);
@@ -352,6 +382,7 @@ def main():
     x = kda_synth.config(args.config)
     r = time_config(x, args.steps, args.warmup, device, hip)
     main_s = summarize(x, r)
+    main_s["graph_replay_us"] = time_graph(x, args.steps, args.warmup, device)
     progress(f"config{args.config}: {main_s}")
 
     # Dominant kernel: the recurrence kernel (the serial chain). It runs once per call in
