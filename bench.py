@@ -282,9 +282,9 @@ def summarize(x, r):
     tot_us = r["ms_per_step"] * 1e3
     alg_bytes = th * BYTES_PER_TOKEN_HEAD_BF16 * es // 2 + state_b
     alg_flop = th * (FLOP_REC_PER_TOKEN_HEAD + FLOP_PREP_PER_TOKEN_HEAD)
-    if x.T == 1 and x.cu_seqlens is None:
-        # Single-token form: one kernel (timed between the first two events), bound by
-        # the state read and write.
+    if 1 <= x.T <= 8 and x.cu_seqlens is None:
+        # Token-loop form (a decode step or a few draft tokens): one kernel (timed between
+        # the first two events), bound by the state read and write.
         return dict(
             us=round(tot_us, 2), tokens_per_s=round(x.tokens() / (tot_us * 1e-6), 1),
             decode_kernel_us=round(prep_us, 2), state_bytes=state_b, alg_bytes=alg_bytes,
@@ -422,6 +422,13 @@ def main():
         per_config["decode_B256_H32"] = summarize(
             xd, time_config(xd, max(10, args.steps // 2), 3, device, hip))
         progress(f"decode: {per_config['decode_B256_H32']}")
+        del xd
+        torch.cuda.empty_cache()
+        # Verification of 4 draft tokens per sequence, same sizes.
+        xd = kda_synth.config(2, B=256, T=4, H=32)
+        per_config["draft4_B256_H32"] = summarize(
+            xd, time_config(xd, max(10, args.steps // 2), 3, device, hip))
+        progress(f"draft4: {per_config['draft4_B256_H32']}")
         del xd
         torch.cuda.empty_cache()
     # Fractions against the rates measured on this machine as well as the published peaks.

@@ -143,10 +143,12 @@ struct Plan {
   size_t total = 0;
 };
 
-// One token per sequence (fixed layout, no checkpoints): the single-token kernel, no
-// workspace.
+// A few tokens per sequence (fixed layout, 1 <= T <= kDecodeMaxT, no checkpoints,
+// automatic geometry): the token-loop kernel, no workspace. An explicit
+// rows_per_workgroup or segment_chunks asks for the chunked path.
 bool decode_form(const kda_prefill_args* a) {
-  return a->T == 1 && !a->cu_seqlens && a->checkpoint_every == 0;
+  return a->T >= 1 && a->T <= kda::kDecodeMaxT && !a->cu_seqlens &&
+         a->checkpoint_every == 0 && a->rows_per_workgroup == 0 && a->segment_chunks == 0;
 }
 
 Plan make_plan(const kda_prefill_args* a) {

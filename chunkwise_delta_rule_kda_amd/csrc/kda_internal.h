@@ -21,6 +21,11 @@ constexpr int32_t kModeSerial = 0;
 constexpr int32_t kModeScanA = 1;  // segment 0 (true start) + Z_p, Phi_p of later segments
 constexpr int32_t kModeScanC = 2;  // segments 1..P-1 again from their true start states
 
+// Longest fixed-layout sequence the token-loop kernel takes (automatic geometry, no
+// checkpoints); longer calls use the chunked path, which was faster from 16 tokens on
+// at every shape measured (8 tokens: the token loop by 1.2-1.3x).
+constexpr int kDecodeMaxT = 8;
+
 // Chunks per workgroup of the scan-output launch (affine-output segmented form).
 constexpr int kScanOutChunks = 4;
 

@@ -13,9 +13,12 @@
  * kernel and a serial recurrence kernel whose 128 value rows are split across compute
  * units (section 3.1 of the same post: value rows never interact).
  *
- * One token per sequence (T = 1 in the fixed layout, no checkpoints) is a decode step:
- * a single-token kernel reads each state once, updates it in registers and writes it
- * back; such a call needs no workspace (kda_prefill_workspace_bytes returns 0).
+ * A few tokens per sequence (fixed layout with 1 <= T <= 8, no checkpoints, automatic
+ * geometry: rows_per_workgroup = segment_chunks = 0) is a decode step (T = 1) or the
+ * verification of draft tokens: a token-loop kernel reads each state once, applies the
+ * T token steps in registers and writes it back; such a call needs no workspace
+ * (kda_prefill_workspace_bytes returns 0). An explicit rows_per_workgroup or
+ * segment_chunks selects the chunked path for any T.
  *
  * The calling contract follows the "flashinfer.kda_prefill" API page (sections
  * "Optimized Blackwell prefill subset", "SM120a prefill subset" and "State and graph
@@ -287,7 +290,7 @@ typedef struct kda_plan_info {
                                       affine-output form */
   size_t scan_state_offset;
   size_t scan_transition_offset;
-  int32_t decode;                  /* 1: one token per sequence, the single-token kernel */
+  int32_t decode;                  /* 1: the token-loop kernel (1 <= T <= 8, see above) */
   int32_t scan_affine_output;      /* 1: the affine-output segmented form */
   size_t scan_output_offset;
 } kda_plan_info;

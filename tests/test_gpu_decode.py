@@ -1,6 +1,7 @@
-"""One token per sequence (T = 1, fixed layout): the single-token kernel vs the FP64
-oracle (the token recurrence itself), including the in-kernel transforms, FP32 I/O, the
-state pool, and a multi-step decode that must agree with a prefill over the same tokens.
+"""A few tokens per sequence (fixed layout, 1 <= T <= 8): the token-loop kernel vs the
+FP64 oracle (the token recurrence itself), including the in-kernel transforms, FP32 I/O,
+the state pool, the chunked path on the same inputs, and step-by-step decoding (one and
+three tokens per call) that must agree with a prefill over the same tokens.
 Bound: max|err| / max|ref| <= 2e-2."""
 
 import numpy as np
@@ -35,13 +36,19 @@ def check(x, name, **kw):
     assert eo <= TOL and es <= TOL
 
 
-def test_plan_uses_the_single_token_kernel():
+def test_plan_uses_the_token_loop_kernel():
     import chunkwise_delta_rule_kda_amd as kda
 
-    a = kda.make_args(B=64, T=1, H=8, N=64)
-    assert kda.kda_prefill_plan(a)["decode"] == 1
-    assert kda.kda_prefill_workspace_bytes(a) == 0
-    assert kda.kda_prefill_plan(kda.make_args(B=64, T=2, H=8, N=64))["decode"] == 0
+    plan = lambda **kw: kda.kda_prefill_plan(kda.make_args(B=64, H=8, N=64, **kw))
+    for T in (1, 2, 8):
+        a = kda.make_args(B=64, T=T, H=8, N=64)
+        assert kda.kda_prefill_plan(a)["decode"] == 1, T
+        assert kda.kda_prefill_workspace_bytes(a) == 0
+    assert plan(T=9)["decode"] == 0
+    # explicit geometry, or checkpoints, select the chunked path
+    assert plan(T=4, rows_per_workgroup=64)["decode"] == 0
+    assert plan(T=4, segment_chunks=-1)["decode"] == 0
+    assert plan(T=4, checkpoint_every=16)["decode"] == 0
 
 
 @pytest.mark.parametrize("B,H", [(1, 1), (5, 3), (64, 8)])
@@ -53,19 +60,40 @@ def test_fp32():
     check(kda_synth.config(0, T=1, B=4), "config0 fp32")
 
 
-def test_transforms_gate_l2_beta_logit():
-    # config 4's raw-gate recipe with every sequence one token long, as a fixed layout
-    x = kda_synth.config(4, H=3, lengths=[1] * 6)
-    f = lambda a: a.reshape((6, 1) + a.shape[2:])
+@pytest.mark.parametrize("T,B,H", [(2, 5, 3), (5, 8, 4), (8, 3, 2)])
+def test_draft_tokens_with_initial_state(T, B, H):
+    check(kda_synth.config(2, T=T, H=H, B=B), f"config2 T={T} B={B} H={H}")
+
+
+def test_draft_tokens_fp32_weak_decay():
+    check(kda_synth.stress("weak_decay", T=7, H=2, B=2, dtype="fp32"), "weak decay fp32 T=7")
+
+
+def test_token_loop_agrees_with_chunked_path():
+    x = kda_synth.config(2, T=8, H=3, B=4)
+    o1, s1, _ = run_gpu(x)                          # token loop
+    o2, s2, _ = run_gpu(x, rows_per_workgroup=64)   # prepare + recurrence
+    o_ref, s_ref = run_oracle(x)
+    for o, s in ((o1, s1), (o2, s2)):
+        assert rel_err(o, o_ref) <= TOL and rel_err(s, s_ref) <= TOL
+    assert rel_err(o1, o2) <= TOL and rel_err(s1, s2) <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 7])
+def test_transforms_gate_l2_beta_logit(T):
+    # config 4's raw-gate recipe with every sequence T tokens long, as a fixed layout
+    x = kda_synth.config(4, H=3, lengths=[T] * 6)
+    f = lambda a: a.reshape((6, T) + a.shape[2:])
     y = kda_synth.KdaInputs(
         name="decode-transforms", q=f(x.q), k=f(x.k), v=f(x.v), g=f(x.g), beta=f(x.beta),
         state0=x.state0, dtype=x.dtype, state_dtype=x.state_dtype, A_log=x.A_log,
         dt_bias=x.dt_bias, lower_bound=x.lower_bound, l2norm_qk=x.l2norm_qk,
         beta_is_logit=x.beta_is_logit)
-    check(y, "transforms")
+    check(y, f"transforms T={T}")
 
 
-def test_steps_equal_prefill():
+@pytest.mark.parametrize("step", [1, 3])
+def test_steps_equal_prefill(step):
     import torch
 
     import chunkwise_delta_rule_kda_amd as kda
@@ -76,8 +104,8 @@ def test_steps_equal_prefill():
     q, k, v, g, beta = (d.pop(n) for n in ("q", "k", "v", "g", "beta"))
     st = d.pop("state_in").clone()
     outs = []
-    for t in range(x.T):
-        sl = lambda a: a[:, t:t + 1].contiguous()
+    for t in range(0, x.T, step):
+        sl = lambda a: a[:, t:t + step].contiguous()
         o, _ = kda.kda_prefill(sl(q), sl(k), sl(v), sl(g), sl(beta), st, state_out=st, **d)
         outs.append(o)
     torch.cuda.synchronize()
@@ -92,7 +120,7 @@ def test_state_pool():
     import chunkwise_delta_rule_kda_amd as kda
     from oracle import kda_recurrence_fp64
 
-    x = kda_synth.config(2, T=1, H=2, B=3)
+    x = kda_synth.config(2, T=3, H=2, B=3)
     d = to_device(x)
     q, k, v, g, beta = (d.pop(n) for n in ("q", "k", "v", "g", "beta"))
     d.pop("state_in")

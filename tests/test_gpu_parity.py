@@ -103,7 +103,10 @@ def test_varlen_equals_separate_calls_bitwise():
             name="seq", q=x.q[:, a:b], k=x.k[:, a:b], v=x.v[:, a:b], g=x.g[:, a:b],
             beta=x.beta[:, a:b], state0=x.state0[n:n + 1], A_log=x.A_log, dt_bias=x.dt_bias,
             lower_bound=x.lower_bound, l2norm_qk=True, beta_is_logit=True)
-        on, sn, _ = run_gpu(xn)
+        # Explicit geometry keeps a short sequence on the chunked path (a call of 8 or
+        # fewer tokens would otherwise take the token-loop kernel, which rounds
+        # differently); the row choice never changes results.
+        on, sn, _ = run_gpu(xn, rows_per_workgroup=64)
         assert np.array_equal(o[:, a:b], on), n
         assert np.array_equal(s[n], sn[0]), n
 
