@@ -151,8 +151,8 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(Params p) {
         sq += q[e] * q[e];
         sk += k[e] * k[e];
       }
-      const float iq = 1.0f / sqrtf(row_sum16(sq) + 1e-6f);
-      const float ik = 1.0f / sqrtf(row_sum16(sk) + 1e-6f);
+      const float iq = rsqrtf(row_sum16(sq) + 1e-6f);
+      const float ik = rsqrtf(row_sum16(sk) + 1e-6f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         q[e] *= iq;

@@ -203,6 +203,13 @@ __global__ __launch_bounds__(256, 8) void kda_prepare_kernel(Params p) {
   RawRow<BF16> rq, rk, rg;
   float rbeta;
   load_rows<BF16>(p, span, h, r, cq, tid, rq, rk, rg, rbeta);
+  // The gate's per-head parameters, loaded with the rows (independent of them).
+  float gate_a = 0.f, dtb[8];
+  if (p.flags & kFlagGate) {
+    gate_a = p.A_log[h];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dtb[e] = p.dt_bias[h * kD + cq + e];
+  }
   const int64_t valid = span.valid;
   unsigned char* rec = p.records + (h * p.max_chunks + gc) * (int64_t)kRecord;
 
@@ -236,8 +243,8 @@ __global__ __launch_bounds__(256, 8) void kda_prepare_kernel(Params p) {
     lds_barrier();
     sq = sNorm[0][0][r] + sNorm[0][1][r] + sNorm[0][2][r] + sNorm[0][3][r];
     sk = sNorm[1][0][r] + sNorm[1][1][r] + sNorm[1][2][r] + sNorm[1][3][r];
-    const float iq = 1.0f / sqrtf(sq + 1e-6f);
-    const float ik = 1.0f / sqrtf(sk + 1e-6f);
+    const float iq = rsqrtf(sq + 1e-6f);
+    const float ik = rsqrtf(sk + 1e-6f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       q[e] *= iq;
@@ -245,10 +252,9 @@ __global__ __launch_bounds__(256, 8) void kda_prepare_kernel(Params p) {
     }
   }
   if ((p.flags & kFlagGate) && tv) {
-    const float a = __expf(p.A_log[h]);
+    const float a = __expf(gate_a);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      g[e] = p.lower_bound * sigmoidf_(a * (g[e] + p.dt_bias[h * kD + cq + e]));
+    for (int e = 0; e < 8; ++e) g[e] = p.lower_bound * sigmoidf_(a * (g[e] + dtb[e]));
   }
 
   // ---- prefix decay (row scan over tokens) and the decayed key/query rows ----------
