@@ -189,7 +189,11 @@ Plan make_plan(const kda_prefill_args* a) {
       }
     }
   }
-  pl.header = a->cu_seqlens ? round_up(static_cast<size_t>(a->N + 1) * 16, 256) : 0;
+  // varlen header: cu_chunks and cu_segs (int64 [N + 1] each), then the automatic
+  // sequence order (int32 [N])
+  pl.header = a->cu_seqlens ? round_up(static_cast<size_t>(a->N + 1) * 16 +
+                                           static_cast<size_t>(a->N) * 4, 256)
+                            : 0;
   pl.records = pl.header;
   size_t end = pl.records + static_cast<size_t>(pl.max_chunks) * static_cast<size_t>(a->H) *
                                 static_cast<size_t>(kda::kRecord);
@@ -443,7 +447,12 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
                                         : a->H * KDA_HEAD_DIM * KDA_HEAD_DIM;
     p.state_out = const_cast<void*>(a->state_in);  // the pool is updated in place
   }
-  p.seq_order = a->seq_order;
+  // Without a caller's order, the serial form starts varlen sequences longest first
+  // (ordered on the device by the plan kernel; up to kAutoOrderMax sequences).
+  int32_t* auto_order = nullptr;
+  if (a->cu_seqlens && pl.seg_len == 0 && !a->seq_order && a->N <= kda::kAutoOrderMax)
+    auto_order = reinterpret_cast<int32_t*>(ws + static_cast<size_t>(a->N + 1) * 16);
+  p.seq_order = a->seq_order ? a->seq_order : auto_order;
   if (a->checkpoint_every > 0) {
     p.ckpt = a->state_checkpoints;
     p.ckpt_cu = a->checkpoint_cu_starts;
@@ -478,7 +487,7 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
     return KDA_OK;
   }
   if (ev) e = hipEventRecord(ev[0], stream);
-  if (e == hipSuccess && a->cu_seqlens) e = kda::launch_plan(p, stream);
+  if (e == hipSuccess && a->cu_seqlens) e = kda::launch_plan(p, auto_order, stream);
   if (e == hipSuccess && a->T > 0) e = kda::launch_prepare(p, io_bf16, stream);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
   if (pl.seg_len == 0) {

@@ -26,6 +26,10 @@ constexpr int32_t kModeScanC = 2;  // segments 1..P-1 again from their true star
 // at every shape measured (8 tokens: the token loop by 1.2-1.3x).
 constexpr int kDecodeMaxT = 8;
 
+// Largest sequence count for which the varlen plan orders the sequences by decreasing
+// length (one workgroup, one sequence per thread).
+constexpr int kAutoOrderMax = 256;
+
 // Chunks per workgroup of the scan-output launch (affine-output segmented form).
 constexpr int kScanOutChunks = 4;
 
@@ -81,7 +85,9 @@ struct Params {
   const int32_t* seq_order;   // [N] or null
 };
 
-hipError_t launch_plan(const Params& p, hipStream_t stream);
+// auto_order: null, or [N] int32 (N <= kAutoOrderMax) for the sequences by decreasing
+// chunk count.
+hipError_t launch_plan(const Params& p, int32_t* auto_order, hipStream_t stream);
 hipError_t launch_prepare(const Params& p, bool io_bf16, hipStream_t stream);
 int recurrence_loader_waves(int compute_waves);
 hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16,

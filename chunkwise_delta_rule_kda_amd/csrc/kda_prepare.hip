@@ -23,11 +23,14 @@ namespace kda {
 // Exclusive prefixes over the packed sequences: cu_chunks[0..N] of ceil(len_n / 16),
 // and, when seg_len > 0, cu_segs[0..N] of max(1, ceil(chunks_n / seg_len)) (the number
 // of time segments of sequence n; a zero-length sequence keeps one empty segment so its
-// state passes through).
+// state passes through). When order is given (N <= kAutoOrderMax), also the sequences
+// by decreasing chunk count, ties by index: the order in which the serial recurrence
+// starts them, so that the longest do not start last.
 __global__ __launch_bounds__(256) void kda_plan_kernel(const int64_t* __restrict__ cu,
                                                         int64_t N, int64_t seg_len,
                                                         int64_t* __restrict__ cu_chunks,
-                                                        int64_t* __restrict__ cu_segs) {
+                                                        int64_t* __restrict__ cu_segs,
+                                                        int32_t* __restrict__ order) {
   __shared__ int64_t buf[2][256];
   __shared__ int64_t carry[2];
   const int t = threadIdx.x;
@@ -66,6 +69,22 @@ __global__ __launch_bounds__(256) void kda_plan_kernel(const int64_t* __restrict
       carry[1] += buf[1][255];
     }
     __syncthreads();
+  }
+  if (order && N <= kAutoOrderMax) {  // uniform
+    __shared__ int64_t cnt[kAutoOrderMax];
+    int64_t c = 0;
+    if (t < N) {
+      const int64_t len = cu[t + 1] - cu[t];
+      c = len > 0 ? (len + kC - 1) / kC : 0;
+      cnt[t] = c;
+    }
+    __syncthreads();
+    if (t < N) {
+      // rank = sequences that come first: more chunks, or as many with a lower index
+      int rank = 0;
+      for (int j = 0; j < N; ++j) rank += (cnt[j] > c) || (cnt[j] == c && j < t);
+      order[rank] = t;
+    }
   }
 }
 
@@ -423,10 +442,10 @@ __global__ __launch_bounds__(256, 8) void kda_prepare_kernel(Params p) {
   }
 }
 
-hipError_t launch_plan(const Params& p, hipStream_t stream) {
+hipError_t launch_plan(const Params& p, int32_t* auto_order, hipStream_t stream) {
   const int64_t seg_len = p.seg_len;  // 0: serial recurrence, no segment prefix
   hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.N,
-                     seg_len, p.cu_chunks, p.cu_segs);
+                     seg_len, p.cu_chunks, p.cu_segs, auto_order);
   return hipGetLastError();
 }
 

@@ -179,9 +179,11 @@ typedef struct kda_prefill_args {
   int64_t state_slot_pitch;
 
   /* Scheduling order (the same page, section "Packed scheduling"): int32 [N] device, a
-     permutation of [0, N) (caller contract, not checked), or NULL for the natural
-     order. The serial form starts the sequences' workgroups in this order, so ordering
-     by decreasing length shortens the last partial wave. Results do not depend on it. */
+     permutation of [0, N) (caller contract, not checked), or NULL. The serial form
+     starts the sequences' workgroups in this order, so ordering by decreasing length
+     shortens the last partial wave. NULL: varlen calls with N <= 256 are ordered that
+     way on the device (the plan kernel), other calls keep the natural order. Results do
+     not depend on it. */
   const int32_t *seq_order;
 
   /* Optional timing hooks (host array of hipEvent_t handles, or NULL). When
@@ -202,7 +204,11 @@ typedef struct kda_prefill_args {
  *                                 prefix of ceil(len_n / 16) (the flashinfer page's
  *                                 compact chunk prefix, section "Packed scheduling"),
  *                                 then int64 cu_segs[N + 1], the prefix of the segment
- *                                 counts max(1, ceil(chunks_n / segment_chunks)).
+ *                                 counts max(1, ceil(chunks_n / segment_chunks)), then
+ *                                 int32 order[N]: in the serial form without a caller's
+ *                                 seq_order (and N <= 256), the sequences by decreasing
+ *                                 chunk count (ties by index), the order in which their
+ *                                 work starts.
  *   [KDA_WS_HEADER, ...)          one KDA_WS_RECORD-byte record per (chunk c, head h)
  *                                 at index h * max_chunks + c, where c counts chunks
  *                                 over all sequences in order and max_chunks is the
@@ -222,7 +228,7 @@ typedef struct kda_prefill_args {
  *                                 2048 elements of the io dtype, Qt Phi^T of each
  *                                 chunk of a later segment (Phi from the segment start
  *                                 to the chunk start), in the record's Qt layout.
- * KDA_WS_HEADER = round_up((N + 1) * 16, 256) for varlen, 0 for the fixed layout.
+ * KDA_WS_HEADER = round_up((N + 1) * 16 + 4 N, 256) for varlen, 0 for the fixed layout.
  *
  * A record holds, for the chunk's 16 tokens (pad tokens of a short last chunk behave as
  * k = q = v = 0, g = 0, beta = 0), with the page's K_start, Q_start, K_end, D_{0:15},

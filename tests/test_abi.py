@@ -231,6 +231,9 @@ def test_plan_segments_small_head_counts():
     assert v["recurrence_workgroups"] == 2 * bound * 4
     assert v["scan_c_workgroups"] == 2 * bound * ((20 + 3) // 4)
     assert v["workspace_header_bytes"] == 256
+    # header: cu_chunks and cu_segs (int64 [N + 1]) and the automatic order (int32 [N])
+    big = kda.kda_prefill_plan(fake(H=2, T=4000, N=100, varlen=True), 256)
+    assert big["workspace_header_bytes"] == ((101 * 16 + 100 * 4 + 255) // 256) * 256
     assert status(fake(segment_chunks=1 << 25)) == 10
 
 

@@ -121,3 +121,25 @@ def test_seq_order_fixed_layout():
     got = kda.kda_prefill(q, k, v, g, beta, segment_chunks=-1, seq_order=so, **d)
     torch.cuda.synchronize()
     assert torch.equal(got[0], base[0]) and torch.equal(got[1], base[1])
+
+
+def test_automatic_order_changes_nothing():
+    # Varlen serial calls without a seq_order start the sequences longest first (ordered
+    # on the device); the results equal those of the natural order bitwise.
+    import torch
+
+    import chunkwise_delta_rule_kda_amd as kda
+    from kda_testlib import run_oracle
+
+    x = kda_synth.config(4, H=2, lengths=[5, 300, 40, 0, 170, 33])
+    d = to_device(x)
+    q, k, v, g, beta = (d.pop(n) for n in ("q", "k", "v", "g", "beta"))
+    auto = kda.kda_prefill(q, k, v, g, beta, segment_chunks=-1, **d)
+    ident = torch.arange(x.N, dtype=torch.int32, device="cuda")
+    nat = kda.kda_prefill(q, k, v, g, beta, segment_chunks=-1, seq_order=ident, **d)
+    torch.cuda.synchronize()
+    assert torch.equal(auto[0], nat[0]) and torch.equal(auto[1], nat[1])
+    o_ref, s_ref = run_oracle(x)
+    assert rel_err(auto[0].float().cpu().numpy(), o_ref) <= 2e-2
+    assert rel_err(auto[1].float().cpu().numpy(), s_ref) <= 2e-2
+
