@@ -215,10 +215,11 @@ Plan make_plan(const kda_prefill_args* a) {
 
 size_t workspace_need(const kda_prefill_args* a) { return make_plan(a).total; }
 
-// Workgroups of launches A and C of the segmented form. Fixed layout: the active row
-// blocks only (per sequence b0 for segment 0 and 2 b0 for each of segments 1 .. P-2 in
-// A, b0 for each of segments 1 .. P-1 in C, b0 = 128 / rows). Varlen: every scan slot
-// of the bound times the row blocks; workgroups past a sequence's segments exit.
+// Workgroups of launch A and of the re-run launch C of the segmented form. Fixed
+// layout: the active row blocks only (per sequence b0 for segment 0 and 2 b0 for each of
+// segments 1 .. P-1 (affine-output form) or 1 .. P-2 (re-run form) in A, b0 for each of
+// segments 1 .. P-1 in C, b0 = 128 / rows). Varlen: every scan slot of the bound times
+// the row blocks; workgroups past a sequence's segments exit.
 int64_t scan_a_workgroups(const kda_prefill_args* a, const Plan& pl, int rows) {
   const int64_t b0 = KDA_HEAD_DIM / rows;
   if (a->cu_seqlens) return a->H * pl.seg_stride * 2 * b0;

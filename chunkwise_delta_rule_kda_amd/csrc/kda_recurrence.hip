@@ -22,12 +22,21 @@
 // Segments. The carry is affine in the state: over a run of chunks, S_end = S_start Phi
 // + Z, where Z is the end state of the run started from zero and Phi (128 x 128, keys x
 // keys) the end state of the run started from the identity with V = 0 (rows of S never
-// interact, so Phi's rows are computed exactly like value rows). A sequence cut into
-// segments 0..P-1 of L chunks is evaluated in three launches:
+// interact, so Phi's rows are computed exactly like value rows). The output is affine
+// in the start state too: inside segment p, O_c = O^Z_c + (Qt_c Phi_{p,c}^T) S_p^T, where
+// O^Z_c is the zero-start run's output and Qt_c Phi_{p,c}^T what the transition run
+// outputs (its V is zero). A sequence cut into segments 0..P-1 of L chunks is evaluated
+// in three launches (the affine-output form):
 //   A: segment 0 from the true initial state (writing its O and S_1), and, for
-//      segments 1..P-2, Z_p and Phi_p;
-//   B: S_{p+1} = S_p Phi_p + Z_p for p = 1..P-2 (kda_combine_kernel);
-//   C: segments 1..P-1 again from S_p, writing O and, for the last one, the final state.
+//      segments 1..P-1, Z_p and O^Z (into o) and Phi_p and Qt Phi^T (into scan_q);
+//   B: S_{p+1} = S_p Phi_p + Z_p for p = 1..P-1 (kda_combine_kernel), the last step
+//      giving the final state;
+//   C: o += (Qt Phi^T) S_p^T for every chunk of segments 1..P-1, in parallel
+//      (kda_scan_output_kernel).
+// Calls with state checkpoints need the states inside the later segments and take the
+// re-run form instead: A computes Z_p and Phi_p of segments 1..P-2 only, B stops at
+// S_{P-1}, and C runs segments 1..P-1 again from S_p with this kernel, writing O, the
+// checkpoints and, for the last one, the final state.
 // Workgroups of launch A see a 256-row space: rows 0..127 are value rows (Z or the true
 // run), rows 128..255 the rows of Phi. Serial mode (one segment per sequence) is the
 // single launch of the plain recurrence.
@@ -296,7 +305,7 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
   const int64_t seg = gsg - first;
   const int vr = blk * rows;
   if (p.mode == kModeScanA) {
-    if (!p.affine_out && nseg >= 2 && seg == nseg - 1) return false;  // only in launch C
+    if (!p.affine_out && nseg >= 2 && seg == nseg - 1) return false;  // only in the re-run
     if (vr >= kD && seg == 0) return false;           // no transition for segment 0
   } else if (seg == 0) {
     return false;                                     // segment 0: only in launch A
@@ -346,7 +355,7 @@ __device__ bool segment_task(const Params& p, Task& t, int64_t h, int64_t n, int
     }
     return true;
   }
-  // launch C
+  // launch C of the re-run form
   t.vwg = vr;
   t.start = kStartScan;
   t.s_src = p.scan_s + slot * (kD * kD);
