@@ -319,6 +319,7 @@ def main():
     ap.add_argument("--extra-configs", default="0,2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step line")
+    ap.add_argument("--no-head-sweep", action="store_true", help="skip the H=24/48 lines")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter "
                          "calibration for rocprofv3 --pmc runs)")
@@ -431,6 +432,15 @@ def main():
         progress(f"draft4: {per_config['draft4_B256_H32']}")
         del xd
         torch.cuda.empty_cache()
+    # The pages' other head counts at T=8192 (config 1's recipe), for the scaling curve.
+    if not args.no_head_sweep:
+        for hh in (24, 48):
+            xh = kda_synth.config(1, H=hh)
+            per_config[f"H{hh}_T8192"] = summarize(
+                xh, time_config(xh, max(5, args.steps // 5), 2, device, hip))
+            progress(f"H={hh}: {per_config[f'H{hh}_T8192']}")
+            del xh
+            torch.cuda.empty_cache()
     # Fractions against the rates measured on this machine as well as the published peaks.
     for v in per_config.values():
         if isinstance(v, dict) and "alg_bytes" in v:
