@@ -703,17 +703,30 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
   if (t.phi_dst) {
     // This lane holds Phi[r][16 b + 4 grp + j] for row r = v0 + m: key r of output
     // key 16 b + m' (m' = 4 grp + j) sits in group kk = r / 32, lane 16 grp' + m',
-    // element e with r % 32 = 16 (e / 4) + 4 grp' + e % 4.
+    // element e with r % 32 = 16 (e / 4) + 4 grp' + e % 4. This wave's 16 rows fill
+    // elements 4 h .. 4 h + 3 (h = v0 / 16 % 2) of every (b, lane) piece of group kk: the
+    // values go through this wave's 4 KB of ring slot (nch + 1) % 3 ([b 8][lane 64][4]),
+    // then out as one 8-byte store per lane and b. Every wave has finished with that slot
+    // once past barrier B_{nch-1} (its last reads were consumed in iteration nch - 2);
+    // an empty run never touched the ring.
+    lds_u8* stage = ring + ((nch + 1) % kSlots) * T::SLOT + wave * 4096;
     const int r = v0 + m;
-    const int kk = r >> 5, q = r & 31;
-    const int e = 4 * (q >> 4) + (q & 3);
-    const int grpp = (q & 15) >> 2;
+    const int kk = r >> 5;
+    const int h = (r >> 4) & 1;
+    const int grpp = (r & 15) >> 2;
 #pragma unroll
     for (int b = 0; b < 8; ++b)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        t.phi_dst[((b * 4 + kk) * 64 + 16 * grpp + 4 * grp + j) * 8 + e] =
+        *reinterpret_cast<__attribute__((address_space(3))) unsigned short*>(
+            stage + ((b * 64 + 16 * grpp + 4 * grp + j) * 4 + (r & 3)) * 2) =
             float_to_bf16_bits(st[b][j]);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const u32x2 piece =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(stage + (b * 64 + lane) * 8);
+      *reinterpret_cast<u32x2*>(t.phi_dst + ((b * 4 + kk) * 64 + lane) * 8 + 4 * h) = piece;
+    }
   }
 }
 
