@@ -117,17 +117,16 @@ class kda_plan_info(ctypes.Structure):
         ("segment_chunks", ctypes.c_int64),
         ("segments_per_head_bound", ctypes.c_int64),
         ("combine_workgroups", ctypes.c_int64),
-        ("scan_output_workgroups", ctypes.c_int64),
+        ("scan_c_workgroups", ctypes.c_int64),
         ("scan_state_offset", ctypes.c_size_t),
         ("scan_transition_offset", ctypes.c_size_t),
         ("decode", ctypes.c_int32),
+        ("scan_affine_output", ctypes.c_int32),
         ("scan_output_offset", ctypes.c_size_t),
-        ("checkpoint_fixup_workgroups", ctypes.c_int64),
-        ("checkpoint_parts_offset", ctypes.c_size_t),
     ]
 
 
-ABI_VERSION = 7  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
+ABI_VERSION = 6  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
 
 
 def lib_path():

@@ -138,9 +138,8 @@ struct Plan {
   size_t records = 0;        // offset of the records
   size_t scan_s = 0;         // offset of the FP32 scan states
   size_t scan_phi = 0;       // offset of the BF16 transitions
-  size_t scan_q = 0;         // offset of Qt Phi^T per chunk
-  size_t ck_z = 0;           // offset of the checkpoint Z parts (FP32), with checkpoints
-  size_t ck_phi = 0;         // offset of the checkpoint Phi parts (BF16), with checkpoints
+  bool affine = false;       // affine-output segmented form (no checkpoints)
+  size_t scan_q = 0;         // offset of Qt Phi^T per chunk (affine-output form)
   size_t total = 0;
 };
 
@@ -163,11 +162,12 @@ Plan make_plan(const kda_prefill_args* a) {
     L = a->segment_chunks;
   } else if (a->segment_chunks == 0) {
     // Time segments pay off when few (sequence, head) pairs leave compute units idle:
-    // launch A has 4 P - 2 workgroups of 64 rows per pair for P segments; aim for one
-    // per compute unit, with segments of at least 16 chunks.
+    // launch A has 4 P - 2 (affine-output form) or 4 P - 6 (with checkpoints)
+    // workgroups of 64 rows per pair for P segments; aim for one per compute unit,
+    // with segments of at least 16 chunks.
     const int64_t pairs = a->N * a->H;
     if (pairs > 0 && pairs * 8 <= kScanTargetCUs) {
-      const int64_t P = (kScanTargetCUs / pairs + 2) / 4;
+      const int64_t P = (kScanTargetCUs / pairs + (a->checkpoint_every > 0 ? 6 : 2)) / 4;
       if (P >= 2) {
         L = (per_seq + P - 1) / P;
         if (L < 16) L = 16;
@@ -202,14 +202,11 @@ Plan make_plan(const kda_prefill_args* a) {
     pl.scan_s = round_up(end, 256);
     pl.scan_phi = pl.scan_s + slots * kda::kD * kda::kD * 4;
     end = pl.scan_phi + slots * kda::kD * kda::kD * 2;
-    pl.scan_q = round_up(end, 256);
-    end = pl.scan_q + static_cast<size_t>(pl.max_chunks) * static_cast<size_t>(a->H) * 2048 *
-                          elem_size(a->io_dtype);
-    if (a->checkpoint_every > 0 && a->checkpoint_rows > 0) {
-      const size_t parts = static_cast<size_t>(a->checkpoint_rows) * static_cast<size_t>(a->H);
-      pl.ck_z = round_up(end, 256);
-      pl.ck_phi = pl.ck_z + parts * kda::kD * kda::kD * 4;
-      end = pl.ck_phi + parts * kda::kD * kda::kD * 2;
+    pl.affine = a->checkpoint_every == 0;
+    if (pl.affine) {
+      pl.scan_q = round_up(end, 256);
+      end = pl.scan_q + static_cast<size_t>(pl.max_chunks) * static_cast<size_t>(a->H) * 2048 *
+                            elem_size(a->io_dtype);
     }
   }
   pl.total = end;
@@ -218,23 +215,31 @@ Plan make_plan(const kda_prefill_args* a) {
 
 size_t workspace_need(const kda_prefill_args* a) { return make_plan(a).total; }
 
-// Workgroups of launch A of the segmented form. Fixed layout: the active row blocks
-// only (per sequence b0 for segment 0 and 2 b0 for each of segments 1 .. P-1,
-// b0 = 128 / rows). Varlen: every scan slot of the bound times the row blocks;
-// workgroups past a sequence's segments exit.
+// Workgroups of launch A and of the re-run launch C of the segmented form. Fixed
+// layout: the active row blocks only (per sequence b0 for segment 0 and 2 b0 for each of
+// segments 1 .. P-1 (affine-output form) or 1 .. P-2 (re-run form) in A, b0 for each of
+// segments 1 .. P-1 in C, b0 = 128 / rows). Varlen: every scan slot of the bound times
+// the row blocks; workgroups past a sequence's segments exit.
 int64_t scan_a_workgroups(const kda_prefill_args* a, const Plan& pl, int rows) {
   const int64_t b0 = KDA_HEAD_DIM / rows;
   if (a->cu_seqlens) return a->H * pl.seg_stride * 2 * b0;
   const int64_t P = pl.segs_per_seq;
-  return a->H * a->N * (b0 + 2 * b0 * (P - 1));
+  const int64_t mid = pl.affine ? P - 1 : P - 2;  // segments with Z and Phi runs
+  return a->H * a->N * (P >= 2 ? b0 + 2 * b0 * mid : b0);
 }
 
-// Workgroups of the scan-output launch: kScanOutChunks chunks of one later segment
-// each.
+// Workgroups of the scan-output launch (affine-output form): kScanOutChunks chunks of
+// one later segment each.
 int64_t scan_out_workgroups(const kda_prefill_args* a, const Plan& pl) {
   const int64_t groups = (pl.seg_len + kda::kScanOutChunks - 1) / kda::kScanOutChunks;
   if (a->cu_seqlens) return a->H * pl.seg_stride * groups;
   return a->H * a->N * (pl.segs_per_seq - 1) * groups;
+}
+
+int64_t scan_c_workgroups(const kda_prefill_args* a, const Plan& pl, int rows) {
+  const int64_t b0 = KDA_HEAD_DIM / rows;
+  if (a->cu_seqlens) return a->H * pl.seg_stride * b0;
+  return a->H * a->N * (pl.segs_per_seq - 1) * b0;
 }
 
 // Rows per workgroup of the recurrence launches: the explicit choice, else 64 in the
@@ -379,13 +384,11 @@ kda_status kda_prefill_plan(const kda_prefill_args* a, int32_t num_cus, kda_plan
   out->segments_per_head_bound = pl.seg_stride;
   if (pl.seg_len > 0) {
     out->recurrence_workgroups = scan_a_workgroups(a, pl, rows);
-    out->scan_output_workgroups = scan_out_workgroups(a, pl);
+    out->scan_c_workgroups =
+        pl.affine ? scan_out_workgroups(a, pl) : scan_c_workgroups(a, pl, rows);
     out->combine_workgroups = (a->H * a->N + 7) / 8 * 64;
+    out->scan_affine_output = pl.affine ? 1 : 0;
     out->scan_output_offset = pl.scan_q;
-    if (pl.ck_z) {
-      out->checkpoint_fixup_workgroups = a->checkpoint_rows * a->H * 8;
-      out->checkpoint_parts_offset = pl.ck_z;
-    }
   } else {
     out->recurrence_workgroups = (a->N * a->H + 7) / 8 * 8 * (KDA_HEAD_DIM / rows);
   }
@@ -460,11 +463,8 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   if (pl.seg_len > 0) {
     p.scan_s = reinterpret_cast<float*>(ws + pl.scan_s);
     p.scan_phi = reinterpret_cast<unsigned short*>(ws + pl.scan_phi);
-    p.scan_q = ws + pl.scan_q;
-    if (pl.ck_z) {
-      p.ck_z = reinterpret_cast<float*>(ws + pl.ck_z);
-      p.ck_phi = reinterpret_cast<unsigned short*>(ws + pl.ck_phi);
-    }
+    p.affine_out = pl.affine ? 1 : 0;
+    if (pl.affine) p.scan_q = ws + pl.scan_q;
   }
   const bool io_bf16 = a->io_dtype == KDA_BF16;
   const bool st_bf16 = a->state_dtype == KDA_BF16;
@@ -502,11 +502,16 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
     p.blocks = 2 * KDA_HEAD_DIM / rows;
     if (e == hipSuccess) e = recurrence(scan_a_workgroups(a, pl, rows));
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[3], stream);
-    if (e == hipSuccess && (a->cu_seqlens || pl.segs_per_seq >= 2))
+    if (e == hipSuccess && (a->cu_seqlens || pl.segs_per_seq >= (pl.affine ? 2 : 3)))
       e = kda::launch_combine(p, st_bf16, stream);
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[4], stream);
-    if (e == hipSuccess && pl.ck_z) e = kda::launch_ckpt_fixup(p, st_bf16, stream);
-    if (e == hipSuccess) e = kda::launch_scan_output(p, scan_out_workgroups(a, pl), io_bf16, stream);
+    p.mode = kda::kModeScanC;
+    p.blocks = KDA_HEAD_DIM / rows;
+    if (pl.affine) {
+      if (e == hipSuccess) e = kda::launch_scan_output(p, scan_out_workgroups(a, pl), io_bf16, stream);
+    } else {
+      if (e == hipSuccess) e = recurrence(scan_c_workgroups(a, pl, rows));
+    }
   }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s", hipGetErrorString(e));

@@ -15,10 +15,11 @@ constexpr int kOffKeT = 8192;    // bf16 [bp 4][L 64][half 2][j 4]
 constexpr int kOffD = 12288;     // fp32 [L 64][2] (row-broadcast order)
 constexpr int kOffMbAq = 12800;  // bf16 [L 64][Mb 4, A_qk 4]
 
-// Recurrence launch modes: one serial run per sequence, or the first launch of the
+// Recurrence launch modes: one serial run per sequence, or the launches of the
 // segmented (time-parallel) form.
 constexpr int32_t kModeSerial = 0;
 constexpr int32_t kModeScanA = 1;  // segment 0 (true start) + Z_p, Phi_p of later segments
+constexpr int32_t kModeScanC = 2;  // segments 1..P-1 again from their true start states
 
 // Longest fixed-layout sequence the token-loop kernel takes (automatic geometry, no
 // checkpoints); longer calls use the chunked path, which was faster from 16 tokens on
@@ -58,7 +59,7 @@ struct Params {
   uint32_t flags;
   int32_t waves;              // recurrence compute waves per workgroup (16 rows each)
   // Segmented form (modes A and C and the combine kernel).
-  int32_t mode;               // kModeSerial / kModeScanA
+  int32_t mode;               // kModeSerial / kModeScanA / kModeScanC
   int32_t blocks;             // row blocks per task of this launch (A: 256 / rows, C: 128 / rows)
   int64_t seg_len;            // chunks per segment
   int64_t segs_per_seq;       // fixed layout: segments per sequence
@@ -66,14 +67,12 @@ struct Params {
   int64_t* cu_segs;           // varlen: [N + 1] prefix of segments per sequence
   float* scan_s;              // FP32 [H][seg_stride][128][128]: S_p, Z_p
   unsigned short* scan_phi;   // BF16 [H][seg_stride][128 keys][128 rows]: Phi_p transposed
-  // Launch A writes O of the zero-start runs into o and O of the transition runs
-  // (Qt Phi^T per chunk) into scan_q; the combine's last step writes the final state;
-  // the scan-output launch then adds (Qt Phi^T) S_p^T to o.
+  // Affine-output form: launch A also runs segment P-1 and writes O of the zero-start
+  // runs into o and O of the transition runs (Qt Phi^T per chunk) into scan_q; the
+  // combine's last step writes the final state; the scan-output launch then adds
+  // (Qt Phi^T) S_p^T to o instead of rerunning the segments.
+  int32_t affine_out;
   void* scan_q;               // IO dtype [H][max_chunks][kb 4][lane 64][8]
-  // With checkpoints: Z_{p,c} (FP32 state fragments) and Phi_{p,c} (BF16 A-operand
-  // fragments) per [checkpoint row][H] for the checkpoint fix-up.
-  float* ck_z;
-  unsigned short* ck_phi;
   // State checkpoints (ckpt_every chunks apart; 0 = none).
   void* ckpt;                 // [ckpt_rows][H][128][128] of the state dtype
   const int64_t* ckpt_cu;     // [N + 1] row offsets
@@ -94,7 +93,6 @@ int recurrence_loader_waves(int compute_waves);
 hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16,
                              bool state_bf16, hipStream_t stream);
 hipError_t launch_combine(const Params& p, bool state_bf16, hipStream_t stream);
-hipError_t launch_ckpt_fixup(const Params& p, bool state_bf16, hipStream_t stream);
 hipError_t launch_scan_output(const Params& p, int64_t workgroups, bool io_bf16,
                               hipStream_t stream);
 hipError_t launch_decode(const Params& p, bool io_bf16, bool state_bf16, hipStream_t stream);

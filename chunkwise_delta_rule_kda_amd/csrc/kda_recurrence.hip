@@ -135,7 +135,7 @@ __device__ __forceinline__ int64_t state_frag(int rb, int b, int lane) {
 }
 
 // Where one workgroup's run starts, what it reads and what it writes.
-enum StartKind : int { kStartIn = 0, kStartZero = 1, kStartIdentity = 2 };
+enum StartKind : int { kStartIn = 0, kStartZero = 1, kStartIdentity = 2, kStartScan = 3 };
 
 struct Task {
   int64_t tok0;       // first token of the run (row index into [B*T] / packed tokens)
@@ -149,7 +149,9 @@ struct Task {
   int vwg;            // first row of the workgroup within its 128-row space
   int start;          // StartKind
   bool vzero;         // V = 0 (rows of Phi)
+  bool out;           // write O
   bool final_state;   // write state_out
+  const float* s_src; // kStartScan: FP32 [128][128] start state
   float* s_dst;       // FP32 [128][128] end state (scan), or null
   unsigned short* phi_dst;  // BF16 [128 keys][128 rows] end state transposed, or null
 };
@@ -211,7 +213,9 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
   const int64_t task = task_index();
   const int64_t H = p.H;
   t.vzero = false;
+  t.out = true;
   t.final_state = true;
+  t.s_src = nullptr;
   t.s_dst = nullptr;
   t.phi_dst = nullptr;
   if (p.mode == kModeSerial) {
@@ -244,13 +248,16 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
     return true;
   }
   // Fixed layout: only the active row blocks are launched. Per sequence, launch A has
-  // the b0 = 128 / rows value blocks of segment 0, then for segments 1 .. P-1 the b0
-  // value (Z) and b0 transition (Phi) blocks. Varlen: a bound of seg_stride slots x
+  // the b0 = 128 / rows value blocks of segment 0, then for segments 1 .. P-2 (1 .. P-1
+  // in the affine-output form) the b0 value (Z) and b0 transition (Phi) blocks; launch
+  // C the b0 value blocks of segments 1 .. P-1. Varlen: a bound of seg_stride slots x
   // p.blocks per head, decoded below.
   if (!p.cu_seqlens) {
     const int b0 = kD / rows;
     const int64_t P = p.segs_per_seq;
-    const int64_t per_seq = P >= 1 ? b0 + 2 * b0 * (P - 1) : 0;
+    const int64_t mid = p.affine_out ? P - 1 : P - 2;  // segments with Z and Phi runs
+    const int64_t per_seq = p.mode == kModeScanA ? (P >= 2 ? b0 + 2 * b0 * mid : b0)
+                                                 : (P - 1) * b0;
     if (per_seq <= 0) return false;
     const int64_t per_head = p.N * per_seq;
     const int64_t h = task / per_head;
@@ -258,13 +265,21 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
     const int64_t rem = task - h * per_head;
     const int64_t n = rem / per_seq;
     int64_t u = rem - n * per_seq;
-    int64_t seg = 0;
-    if (u >= b0) {
-      u -= b0;
-      seg = 1 + u / (2 * b0);
-      u -= (seg - 1) * 2 * b0;
+    int64_t seg;
+    int vr;
+    if (p.mode == kModeScanA) {
+      if (u < b0) {
+        seg = 0;
+      } else {
+        u -= b0;
+        seg = 1 + u / (2 * b0);
+        u -= (seg - 1) * 2 * b0;
+      }
+    } else {
+      seg = 1 + u / b0;
+      u -= (seg - 1) * b0;
     }
-    const int vr = static_cast<int>(u) * rows;
+    vr = static_cast<int>(u) * rows;
     return segment_task(p, t, h, n, seg, n * P, P, vr);
   }
   const int blocks = p.blocks;
@@ -289,7 +304,12 @@ __device__ bool decode_task(const Params& p, int rows, Task& t) {
   seq_segments(p, n, first, nseg);
   const int64_t seg = gsg - first;
   const int vr = blk * rows;
-  if (vr >= kD && seg == 0) return false;  // no transition for segment 0
+  if (p.mode == kModeScanA) {
+    if (!p.affine_out && nseg >= 2 && seg == nseg - 1) return false;  // only in the re-run
+    if (vr >= kD && seg == 0) return false;           // no transition for segment 0
+  } else if (seg == 0) {
+    return false;                                     // segment 0: only in launch A
+  }
   return segment_task(p, t, h, n, seg, first, nseg, vr);
 }
 
@@ -313,25 +333,33 @@ __device__ bool segment_task(const Params& p, Task& t, int64_t h, int64_t n, int
   t.n = n;
   t.c0s = c0;
   const int64_t slot = h * p.seg_stride + gsg;  // scan slot of this segment
-  if (vr < kD) {
-    // Segment 0 from the true start; a later segment from zero (O^Z into o).
-    t.vwg = vr;
-    t.start = seg == 0 ? kStartIn : kStartZero;
-    t.final_state = nseg == 1;
-    if (nseg >= 2) {
-      // S_1 (segment 0) or Z_seg into slot seg + 1; the last segment's Z into the
-      // sequence's first slot, which never holds a start state.
-      const int64_t zs = seg == nseg - 1 ? h * p.seg_stride + first : slot + 1;
-      t.s_dst = p.scan_s + zs * (kD * kD);
+  if (p.mode == kModeScanA) {
+    if (vr < kD) {
+      t.vwg = vr;
+      t.start = seg == 0 ? kStartIn : kStartZero;
+      t.out = seg == 0 || p.affine_out;  // affine-output form: O of the zero start
+      t.final_state = nseg == 1;
+      if (nseg >= 2) {
+        // S_1 (segment 0) or Z_seg into slot seg + 1; the last segment's Z (affine-output
+        // form only) into the sequence's first slot, which never holds a start state.
+        const int64_t zs = seg == nseg - 1 ? h * p.seg_stride + first : slot + 1;
+        t.s_dst = p.scan_s + zs * (kD * kD);
+      }
+    } else {
+      t.vwg = vr - kD;
+      t.start = kStartIdentity;
+      t.vzero = true;
+      t.out = p.affine_out;  // affine-output form: Qt Phi^T per chunk into scan_q
+      t.final_state = false;
+      t.phi_dst = p.scan_phi + slot * (kD * kD);
     }
-  } else {
-    // Transition run: Phi_seg, and Qt Phi^T per chunk into scan_q.
-    t.vwg = vr - kD;
-    t.start = kStartIdentity;
-    t.vzero = true;
-    t.final_state = false;
-    t.phi_dst = p.scan_phi + slot * (kD * kD);
+    return true;
   }
+  // launch C of the re-run form
+  t.vwg = vr;
+  t.start = kStartScan;
+  t.s_src = p.scan_s + slot * (kD * kD);
+  t.final_state = seg == nseg - 1;
   return true;
 }
 
@@ -376,6 +404,8 @@ __device__ __forceinline__ void read_chain(ChainIn& x, const lds_u8* slot, int l
   }
 }
 
+// OUT: the operands of the output (Qt) are read only by runs that write O.
+template <bool OUT>
 __device__ __forceinline__ void read_tail(TailIn& x, const lds_u8* slot, int lane) {
 #pragma unroll
   for (int bp = 0; bp < 4; ++bp)
@@ -383,9 +413,13 @@ __device__ __forceinline__ void read_tail(TailIn& x, const lds_u8* slot, int lan
         slot + kOffKeT + bp * 1024 + lane * 16);
   x.dv = *reinterpret_cast<const __attribute__((address_space(3))) f32x2*>(slot + kOffD + lane * 8);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    x.qt[kb] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-        slot + kOffQt + kb * 1024 + lane * 16);
+  for (int kb = 0; kb < 4; ++kb) {
+    if constexpr (OUT)
+      x.qt[kb] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+          slot + kOffQt + kb * 1024 + lane * 16);
+    else
+      x.qt[kb] = bf16x8{};
+  }
 }
 
 // Lane N of this lane's 16-lane row (DPP row broadcast).
@@ -418,7 +452,9 @@ __device__ __forceinline__ void state_update(f32x4 (&st)[8], const TailIn& b, i1
   }
 }
 
-// One chunk for one wave: updates the state and returns O[value 4 grp + j][token m].
+// One chunk for one wave: updates the state and returns O[value 4 grp + j][token m]
+// (zero when OUT is false: runs that write no O skip its products).
+template <bool OUT>
 __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f32x4 (&st)[8],
                                             bf16x8 (&sp)[4]) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -435,6 +471,7 @@ __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f
   state_update<0>(st, b, up);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) sp[kb] = pack8(st[2 * kb], st[2 * kb + 1]);
+  if constexpr (!OUT) return zero;
   // O from the entering state (off the chain)
   f32x4 out = mfma32(s0, b.qt[0], zero);
   out = mfma32(s1, b.qt[1], out);
@@ -448,8 +485,13 @@ __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f
 // Unit u = lt + k * LT of a chunk is record byte 16 u (u < 864), V-tile piece u - 864
 // (token row, 16-byte part), or padding (re-reads record unit 0 into the slot's unused
 // tail). Chunks past the run's end re-read its last chunk (in bounds, never used).
-template <bool BF16IO, typename T>
+// OUT false: the record units that hold Qt (whole iterations k of the unit loop, for both
+// loader widths) are neither loaded nor written.
+template <bool BF16IO, typename T, bool OUT>
 __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_u8* ring, int lt) {
+  auto skipped = [](int k) {
+    return !OUT && k * T::LT >= kOffQt / 16 && (k + 1) * T::LT <= (kOffQt + 4096) / 16;
+  };
   const int64_t vstride_b = p.H * kD * T::ES;
   const unsigned char* rec0 =
       p.records + (t.h * p.max_chunks + t.rec_chunk) * static_cast<int64_t>(kRecord);
@@ -488,10 +530,12 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
     if (nvalid >= kC) {
 #pragma unroll
       for (int k = 0; k < T::K; ++k)
-        dst[k] = *reinterpret_cast<const u32x4*>(base[k] + static_cast<uint64_t>(j) * inc[k]);
+        if (!skipped(k))
+          dst[k] = *reinterpret_cast<const u32x4*>(base[k] + static_cast<uint64_t>(j) * inc[k]);
     } else {
 #pragma unroll
       for (int k = 0; k < T::K; ++k) {
+        if (skipped(k)) continue;
         const unsigned char* src = base[k] + static_cast<uint64_t>(j) * inc[k];
         if (vtok[k] >= nvalid) src -= vdrop[k];
         dst[k] = *reinterpret_cast<const u32x4*>(src);
@@ -501,9 +545,11 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
   auto put = [&](const u32x4(&src)[T::K], int slot) {
     lds_u8* s = ring + slot * T::SLOT;
 #pragma unroll
-    for (int k = 0; k < T::K; ++k)
+    for (int k = 0; k < T::K; ++k) {
+      if (skipped(k)) continue;
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(s + (lt + k * T::LT) * 16) =
           src[k];
+    }
   };
 #pragma unroll
   for (int d = 0; d < T::DEPTH; ++d) issue(r[d], d);
@@ -533,28 +579,10 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
   });
 }
 
-// Rows r of a transition state into the combine's A-operand fragments of Phi^T
-// ([b 8][kk 4][lane 64][8] BF16): this lane holds Phi[r][16 b + 4 grp + j], which is key
-// r of output key 16 b + m' (m' = 4 grp + j): group kk = r / 32, lane 16 grp' + m',
-// element e with r % 32 = 16 (e / 4) + 4 grp' + e % 4. One 2-byte store per value (the
-// end-of-run store stages through LDS instead; this one runs inside the chunk loop).
-__device__ __forceinline__ void store_phi_scattered(unsigned short* dst, const f32x4 (&st)[8],
-                                                    int r, int grp) {
-  const int kk = r >> 5, q = r & 31;
-  const int e = 4 * (q >> 4) + (q & 3);
-  const int grpp = (q & 15) >> 2;
-#pragma unroll
-  for (int b = 0; b < 8; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dst[((b * 4 + kk) * 64 + 16 * grpp + 4 * grp + j) * 8 + e] = float_to_bf16_bits(st[b][j]);
-}
-
-// CKPT: the run also writes state checkpoints (a separate instantiation, so that runs
-// without them keep a loop body with no checkpoint test in it): the true run its states,
-// a later segment's zero-start run Z_{p,c} and its transition run Phi_{p,c} (into the
-// workspace; the checkpoint fix-up adds S_p Phi_{p,c} + Z_{p,c}).
-template <bool BF16IO, bool BF16ST, int W, bool CKPT>
+// OUT: the run writes O (and carries the true state); CKPT: it also writes state
+// checkpoints (a separate instantiation, so that runs without them keep a loop body
+// with no checkpoint test in it).
+template <bool BF16IO, bool BF16ST, int W, bool OUT, bool CKPT>
 __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds_u8* ring,
                                              int wave, int lane) {
   using T = Tile<BF16IO, W>;
@@ -572,6 +600,8 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
     const int key = 16 * b + 4 * grp;
     if (t.start == kStartIn && p.state_in && srow >= 0) {
       st[b] = load4<BF16ST>(p.state_in, srow + key);
+    } else if (t.start == kStartScan) {
+      st[b] = load4<false>(t.s_src, state_frag(v0 >> 4, b, lane));
     } else if (t.start == kStartIdentity) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) st[b][j] = (v0 + m == key + j) ? 1.f : 0.f;
@@ -594,8 +624,8 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
     // The O of chunk c is stored in iteration c + 1, after that iteration's MFMA work
     // has been issued, so that its wait for chunk c's last products is hidden.
     f32x4 pend = {0.f, 0.f, 0.f, 0.f};
-    // O[token m][rows v0 + 4 grp + j] goes to o. A transition run writes Qt Phi^T
-    // instead: its rows v0 + 4 grp + j are the keys of that product,
+    // O[token m][rows v0 + 4 grp + j] goes to o. A transition run (affine-output form)
+    // writes Qt Phi^T instead: its rows v0 + 4 grp + j are the keys of that product,
     // stored per chunk in the Qt operand layout [kb 4][lane 64][e 8] of scan_q (key
     // 32 kb + 16 (e / 4) + 4 grp + e % 4 of token m in lane 16 grp + m), which puts
     // this lane's four values in its own lane, block v0 / 32, elements 4 (v0 / 16 % 2) + j.
@@ -612,10 +642,10 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
       if (m < t.tok_end - (t.tok0 + c * kC)) store4<BF16IO>(obuf, ooff + c * ostep, val);
     };
     TailIn tail;
-    read_tail(tail, ring, lane);
-    // State checkpoints: the state before every chunk j of the sequence with
-    // j % ckpt_every == 0 belongs to row ckpt_cu[n] + j / ckpt_every, if that row exists
-    // (for the runs of later segments, its Z and Phi parts).
+    read_tail<OUT>(tail, ring, lane);
+    // State checkpoints (runs that write O are the runs that carry the true state): the
+    // state before every chunk j of the sequence with j % ckpt_every == 0 goes to row
+    // ckpt_cu[n] + j / ckpt_every, if that row exists.
     const int64_t ck_q = CKPT ? p.ckpt_every : 1;
     int64_t ck_c = 0, ck_row = 0;
     if constexpr (CKPT) {
@@ -628,18 +658,9 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
       if constexpr (CKPT) {
         if (c == ck_c) {
           if (ck_row >= 0 && ck_row < p.ckpt_rows) {
-            const int64_t slot = (ck_row * p.H + t.h) * (kD * kD);
-            if (t.start == kStartIn) {  // the true state (uniform branches)
-              const int64_t crow = ((ck_row * p.H + t.h) * kD + v0 + m) * kD;
+            const int64_t crow = ((ck_row * p.H + t.h) * kD + v0 + m) * kD;
 #pragma unroll
-              for (int b = 0; b < 8; ++b) store4<BF16ST>(p.ckpt, crow + 16 * b + 4 * grp, st[b]);
-            } else if (t.start == kStartZero) {  // Z_{p,c}
-#pragma unroll
-              for (int b = 0; b < 8; ++b)
-                store4<false>(p.ck_z + slot, state_frag(v0 >> 4, b, lane), st[b]);
-            } else {  // Phi_{p,c}
-              store_phi_scattered(p.ck_phi + slot, st, v0 + m, grp);
-            }
+            for (int b = 0; b < 8; ++b) store4<BF16ST>(p.ckpt, crow + 16 * b + 4 * grp, st[b]);
           }
           ck_c += ck_q;
           ++ck_row;
@@ -652,22 +673,23 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
       ChainIn nxt;
       TailIn ntail;
       read_chain<BF16IO, W>(nxt, ring + ns * T::SLOT, lane, wave, nvalid_of(c + 1));
-      read_tail(ntail, ring + ns * T::SLOT, lane);
+      read_tail<OUT>(ntail, ring + ns * T::SLOT, lane);
       const f32x4 prev = pend;
-      pend = chunk_step(cur, tail, st, sp);
-      if (c > 0) store_out(c - 1, prev);
+      pend = chunk_step<OUT>(cur, tail, st, sp);
+      if (OUT && c > 0) store_out(c - 1, prev);
       // Keep the reads in this iteration: without these uses the compiler sinks them to
       // the top of the next iteration, right before the MFMA chain that needs them.
       asm volatile("" ::"v"(nxt.kn[0]), "v"(nxt.kn[1]), "v"(nxt.kn[2]), "v"(nxt.kn[3]),
                    "v"(nxt.mb), "v"(nxt.aq), "v"(nxt.vv));
       asm volatile("" ::"v"(ntail.ke[0]), "v"(ntail.ke[1]), "v"(ntail.ke[2]), "v"(ntail.ke[3]),
                    "v"(ntail.dv));
-      asm volatile("" ::"v"(ntail.qt[0]), "v"(ntail.qt[1]), "v"(ntail.qt[2]), "v"(ntail.qt[3]));
+      if constexpr (OUT)
+        asm volatile("" ::"v"(ntail.qt[0]), "v"(ntail.qt[1]), "v"(ntail.qt[2]), "v"(ntail.qt[3]));
       cur = nxt;
       tail = ntail;
       cs = ns;
     }
-    store_out(nch - 1, pend);
+    if (OUT) store_out(nch - 1, pend);
   }
 
   if (t.final_state && p.state_out && srow >= 0) {
@@ -725,8 +747,13 @@ __global__ __launch_bounds__(block_threads(W), 2) void kda_recurrence_kernel(Par
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int lt = static_cast<int>(threadIdx.x) - 64 * W;
-  if (wave < W) compute_loop<BF16IO, BF16ST, W, CK>(p, t, ring, wave, lane);
-  else if (t.nch > 0) loader_loop<BF16IO, T>(p, t, ring, lt);
+  if (t.out) {
+    if (wave < W) compute_loop<BF16IO, BF16ST, W, true, CK>(p, t, ring, wave, lane);
+    else if (t.nch > 0) loader_loop<BF16IO, T, true>(p, t, ring, lt);
+  } else {
+    if (wave < W) compute_loop<BF16IO, BF16ST, W, false, false>(p, t, ring, wave, lane);
+    else if (t.nch > 0) loader_loop<BF16IO, T, false>(p, t, ring, lt);
+  }
 }
 
 // Launch B of the segmented form: S_{p+1} = S_p Phi_p + Z_p, p = 1 .. P-2, for 16 value
@@ -762,7 +789,7 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
   if (h >= p.H) return;
   int64_t first, nseg;
   seq_segments(p, n, first, nseg);
-  const int64_t last = nseg - 1;  // steps s = 1 .. last
+  const int64_t last = p.affine_out ? nseg - 1 : nseg - 2;  // steps s = 1 .. last
   if (last < 1 || first < 0 || first + nseg > p.seg_stride) return;  // nothing to combine
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & 63;
@@ -968,60 +995,6 @@ __global__ __launch_bounds__(256, BF16IO ? 3 : 2) void kda_scan_output_kernel(Pa
   }
 }
 
-// Checkpoint fix-up of the segmented form: a checkpoint row inside a later segment p
-// holds S_p Phi_{p,c} + Z_{p,c}, where launch A wrote Z_{p,c} (state fragments, FP32) and
-// Phi_{p,c} (the combine's A-operand fragments) into the workspace at the row's index,
-// and the combine wrote S_p. One workgroup per (row, head, 16-row block): the combine's
-// step (wave w: output key blocks 2 w, 2 w + 1, eight 16x16x32 products), stored to the
-// row. Rows of segment 0 were written by the true run.
-template <bool BF16ST>
-__global__ __launch_bounds__(256) void kda_ckpt_fixup_kernel(Params p) {
-  const int64_t bid = blockIdx.x;
-  const int rb = static_cast<int>(bid & 7);
-  const int64_t rh = bid >> 3;  // row * H + h
-  const int64_t row = rh / p.H;
-  const int64_t h = rh - row * p.H;
-  if (row >= p.ckpt_rows || row < p.ckpt_cu[0] || row >= p.ckpt_cu[p.N]) return;
-  int64_t lo = 0, hi = p.N - 1;  // largest n with ckpt_cu[n] <= row
-  while (lo < hi) {
-    const int64_t mid = (lo + hi + 1) >> 1;
-    if (p.ckpt_cu[mid] <= row) lo = mid;
-    else hi = mid - 1;
-  }
-  const int64_t n = lo;
-  int64_t start, end, chunk0, nch, first, nseg;
-  seq_range(p, n, start, end, chunk0, nch);
-  seq_segments(p, n, first, nseg);
-  const int64_t c = (row - p.ckpt_cu[n]) * p.ckpt_every;  // chunk within the sequence
-  if (c >= nch) return;
-  const int64_t seg = c / p.seg_len;
-  if (seg < 1 || seg >= nseg || first < 0 || first + nseg > p.seg_stride) return;
-
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int lane = static_cast<int>(threadIdx.x) & 63;
-  const float* sp_src = p.scan_s + (h * p.seg_stride + first + seg) * (kD * kD);
-  const unsigned char* phi =
-      reinterpret_cast<const unsigned char*>(p.ck_phi + rh * (kD * kD)) +
-      (2 * wave * 4 * 64 + lane) * 16;
-  const float* z = p.ck_z + rh * (kD * kD);
-  bf16x8 sb[4];  // B operand: S_p rows 16 rb + m, keys 32 kk ..
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    sb[kk] = pack8(load4<false>(sp_src, state_frag(rb, 2 * kk, lane)),
-                   load4<false>(sp_src, state_frag(rb, 2 * kk + 1, lane)));
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  const int64_t crow = ((row * p.H + h) * kD + 16 * rb + (lane & 15)) * kD;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    f32x4 acc = zero;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc = mfma32(*reinterpret_cast<const bf16x8*>(phi + (i * 4 + kk) * 1024), sb[kk], acc);
-    const f32x4 st = acc + load4<false>(z, state_frag(rb, 2 * wave + i, lane));
-    store4<BF16ST>(p.ckpt, crow + 16 * (2 * wave + i) + 4 * (lane >> 4), st);
-  }
-}
-
 template <bool BF16IO, bool BF16ST, bool CK>
 void launch_waves(const Params& p, dim3 grid, hipStream_t stream) {
   switch (p.waves) {
@@ -1075,16 +1048,6 @@ hipError_t launch_scan_output(const Params& p, int64_t workgroups, bool io_bf16,
   const dim3 grid(static_cast<unsigned>(workgroups));
   if (io_bf16) hipLaunchKernelGGL(kda_scan_output_kernel<true>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(kda_scan_output_kernel<false>, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_ckpt_fixup(const Params& p, bool state_bf16, hipStream_t stream) {
-  const int64_t wgs = p.ckpt_rows * p.H * 8;  // (row, head, 16-row block)
-  if (wgs <= 0) return hipSuccess;
-  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(wgs));
-  if (state_bf16) hipLaunchKernelGGL(kda_ckpt_fixup_kernel<true>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(kda_ckpt_fixup_kernel<false>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 6
 #define KDA_HEAD_DIM 128 /* d_k = d_v = 128 */
 #define KDA_CHUNK 16     /* tokens per chunk */
 
@@ -128,20 +128,22 @@ typedef struct kda_prefill_args {
      segment_chunks, results are bitwise identical for every choice. */
   int32_t rows_per_workgroup;
 
-  /* Time segments of the recurrence. The chunk-to-chunk carry and the outputs are
-     affine in the state, so a sequence can be cut into segments of this many chunks
-     that run in parallel: the first pass runs segment 0 from the true start and, for
-     each later segment, its zero-start run (whose output goes to o) and its transition
-     run Phi (128 x 128; its output Qt Phi^T per chunk goes to the workspace); the
-     segment start states are then combined serially (one 128x128x128 product per
-     segment, the last one giving the final state), and a parallel pass adds
-     (Qt Phi^T) S_p^T to o. State checkpoints inside later segments are formed the same
-     way (S_p Phi + Z, by a fix-up launch). About twice the recurrence work buys a
-     critical path of about one segment plus the combine, which pays off when few
-     (sequence, head) pairs leave compute units idle. 0 = automatic (segments only when
-     N * H <= 32, sized so the first pass has about one workgroup per compute unit of a
-     256-CU device); negative = never (one serial run per sequence); positive = this many
-     chunks per segment. Results differ from the serial form only by rounding. */
+  /* Time segments of the recurrence. The chunk-to-chunk carry is affine in the state,
+     so a sequence can be cut into segments of this many chunks that run in parallel:
+     each later segment's transition Phi (128 x 128) and zero-start run are computed
+     first, and the segment start states are then combined serially (one 128x128x128
+     product per segment). Without checkpoints (the affine-output form) the first pass
+     also writes each later segment's zero-start output into o and the output of its
+     transition run (Qt Phi^T per chunk) into the workspace, the combine's last step
+     writes the final state, and a parallel pass adds (Qt Phi^T) S_p^T to o: a critical
+     path of about one segment plus the combine. With checkpoints every later segment
+     is instead re-run from its true start (the states inside it are needed): about two
+     segments. Either way about twice or three times the recurrence work buys the
+     shorter path, which pays off when few (sequence, head) pairs leave compute units
+     idle. 0 = automatic (segments only when N * H <= 32, sized so the first pass has
+     about one workgroup per compute unit of a 256-CU device); negative = never (one
+     serial run per sequence); positive = this many chunks per segment. Results differ
+     from the serial form only by rounding. */
   int32_t segment_chunks;
 
   /* State checkpoints, as in the "flashinfer.kda_prefill" page's contract (section
@@ -222,15 +224,10 @@ typedef struct kda_prefill_args {
  *                                 [key block 8][key group 4][lane 64][8] with lane
  *                                 16 g + m holding Phi[k][16 b + m] for the keys
  *                                 k = 32 kk + 16 (e / 4) + 4 g + e % 4.
- *   scan_output_offset            segmented form only: [H][max_chunks] pieces of 2048
- *                                 elements of the io dtype, Qt Phi^T of each chunk of a
- *                                 later segment (Phi from the segment start to the
- *                                 chunk start), in the record's Qt layout.
- *   checkpoint_parts_offset       segmented form with checkpoints only: FP32
- *                                 [checkpoint_rows][H] slots of 128 x 128 (the Z part
- *                                 of a checkpoint inside a later segment, state
- *                                 fragments), then BF16 [checkpoint_rows][H] slots of
- *                                 128 x 128 (its Phi part, transition fragments).
+ *   scan_output_offset            affine-output form only: [H][max_chunks] pieces of
+ *                                 2048 elements of the io dtype, Qt Phi^T of each
+ *                                 chunk of a later segment (Phi from the segment start
+ *                                 to the chunk start), in the record's Qt layout.
  * KDA_WS_HEADER = round_up((N + 1) * 16 + 4 N, 256) for varlen, 0 for the fixed layout.
  *
  * A record holds, for the chunk's 16 tokens (pad tokens of a short last chunk behave as
@@ -295,13 +292,13 @@ typedef struct kda_plan_info {
   int64_t segment_chunks;          /* 0: serial form */
   int64_t segments_per_head_bound; /* scan slots per head */
   int64_t combine_workgroups;
-  int64_t scan_output_workgroups;  /* the scan-output launch */
+  int64_t scan_c_workgroups;       /* the re-run launch, or the scan-output launch of the
+                                      affine-output form */
   size_t scan_state_offset;
   size_t scan_transition_offset;
   int32_t decode;                  /* 1: the token-loop kernel (1 <= T <= 8, see above) */
+  int32_t scan_affine_output;      /* 1: the affine-output segmented form */
   size_t scan_output_offset;
-  int64_t checkpoint_fixup_workgroups; /* segmented form with checkpoints, else 0 */
-  size_t checkpoint_parts_offset;  /* segmented form with checkpoints, else 0 */
 } kda_plan_info;
 kda_status kda_prefill_plan(const kda_prefill_args *a, int32_t num_cus, kda_plan_info *out);
 

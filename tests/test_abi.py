@@ -47,7 +47,7 @@ def test_record_size_matches_header():
 
 def test_abi_version_and_status_strings():
     lib = kda.load_library()
-    assert lib.kda_abi_version() == 7
+    assert lib.kda_abi_version() == 6
     for code in range(11):
         assert kda.kda_status_string(code) and kda.kda_status_string(code) != "unknown status"
     assert kda.kda_status_string(99) == "unknown status"
@@ -191,18 +191,17 @@ def test_plan_follows_the_slice_rule():
 
 
 def test_plan_segments_small_head_counts():
-    # H = 6, T = 8192: 512 chunks. Launch A has 4 P - 2 workgroups per pair, so
-    # P = (256 / 6 + 2) / 4 = 11 segments of 47 chunks.
+    # H = 6, T = 8192: 512 chunks. Affine-output form (no checkpoints): launch A has
+    # 4 P - 2 workgroups per pair, so P = (256 / 6 + 2) / 4 = 11 segments of 47 chunks.
     p = kda.kda_prefill_plan(fake(H=6, T=8192), 256)
     assert p["segment_chunks"] == 47 and p["segments_per_head_bound"] == 11
-    assert p["rows_per_workgroup"] == 64
+    assert p["rows_per_workgroup"] == 64 and p["scan_affine_output"] == 1
     # Active row blocks of 64 rows only: segment 0's value rows, then value (Z) and
     # transition (Phi) rows of segments 1 .. 10; the scan-output launch covers segments
     # 1 .. 10 in groups of 4 chunks.
     assert p["recurrence_workgroups"] == 6 * (2 + 4 * 10)
-    assert p["scan_output_workgroups"] == 6 * 10 * ((47 + 3) // 4)
+    assert p["scan_c_workgroups"] == 6 * 10 * ((47 + 3) // 4)
     assert p["combine_workgroups"] == 64  # 8 row blocks x 6 pairs, padded to 8 XCDs
-    assert p["checkpoint_fixup_workgroups"] == 0 and p["checkpoint_parts_offset"] == 0
     records = 512 * 6 * kda.KDA_WS_RECORD
     assert p["scan_state_offset"] == records            # already 256-byte aligned
     slots = 6 * 11
@@ -210,17 +209,13 @@ def test_plan_segments_small_head_counts():
     assert p["scan_output_offset"] == records + slots * 128 * 128 * 6
     need = kda.kda_prefill_workspace_bytes(fake(H=6, T=8192))
     assert need == records + slots * 128 * 128 * 6 + 512 * 6 * 2048 * 2
-    # With checkpoints: the same segments, plus a Z part (FP32) and a Phi part (BF16)
-    # per (checkpoint row, head) and the fix-up launch (row, head, 16-row block).
-    rows = 8
-    c = kda.kda_prefill_plan(fake(H=6, T=8192, checkpoint_every=1024, checkpoint_rows=rows), 256)
-    assert c["segment_chunks"] == 47 and c["segments_per_head_bound"] == 11
+    # With checkpoints every later segment is re-run: 4 P - 6 workgroups per pair in
+    # launch A, P = (256 / 6 + 6) / 4 = 12 segments of 43 chunks.
+    c = kda.kda_prefill_plan(fake(H=6, T=8192, checkpoint_every=1024), 256)
+    assert c["segment_chunks"] == 43 and c["segments_per_head_bound"] == 12
+    assert c["scan_affine_output"] == 0 and c["scan_output_offset"] == 0
     assert c["recurrence_workgroups"] == 6 * (2 + 4 * 10)
-    assert c["checkpoint_fixup_workgroups"] == rows * 6 * 8
-    assert c["checkpoint_parts_offset"] == need
-    assert kda.kda_prefill_workspace_bytes(
-        fake(H=6, T=8192, checkpoint_every=1024, checkpoint_rows=rows)) == \
-        need + rows * 6 * 128 * 128 * 6
+    assert c["scan_c_workgroups"] == 6 * 11 * 2
     # Forced serial, forced length, and no segments for many heads.
     s = kda.kda_prefill_plan(fake(H=6, T=8192, segment_chunks=-1), 256)
     assert s["segment_chunks"] == 0 and s["rows_per_workgroup"] == 16
@@ -234,7 +229,7 @@ def test_plan_segments_small_head_counts():
     assert v["segments_per_head_bound"] == (mc + 19) // 20 + 3
     bound = v["segments_per_head_bound"]
     assert v["recurrence_workgroups"] == 2 * bound * 4
-    assert v["scan_output_workgroups"] == 2 * bound * ((20 + 3) // 4)
+    assert v["scan_c_workgroups"] == 2 * bound * ((20 + 3) // 4)
     assert v["workspace_header_bytes"] == 256
     # header: cu_chunks and cu_segs (int64 [N + 1]) and the automatic order (int32 [N])
     big = kda.kda_prefill_plan(fake(H=2, T=4000, N=100, varlen=True), 256)

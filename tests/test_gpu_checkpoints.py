@@ -1,10 +1,10 @@
 """State checkpoints vs the FP64 oracle (the flashinfer page's checkpoint contract,
 section "State and graph semantics"): every non-empty sequence writes its initial state
 and the states after each whole interval that ends before the sequence does, at rows
-checkpoint_cu_starts[n] + r. Covers the serial and the segmented form (checkpoints in
-segment 0 come from its true run; those inside later segments are S_p Phi + Z, formed
-by the fix-up launch from the parts the zero-start and transition runs write), varlen
-with empty sequences, FP32 state, intervals past the sequence length and the row cap.
+checkpoint_cu_starts[n] + r. Covers the serial and the segmented form (checkpoints come
+from the first segment's run and from the re-run of the others, the form a segmented
+call takes when checkpoints are asked for), varlen with empty sequences, FP32 state,
+intervals past the sequence length and the row cap.
 Bound: max|err| / max|ref| <= 2e-2 over all rows; row 0 of a sequence is its initial
 state exactly."""
 
@@ -57,9 +57,14 @@ def check(x, name, every, **kw):
     for n, L in enumerate(lengths(x)):
         if L > 0:
             assert np.array_equal(ck[starts[n]], s0[n]), n  # row 0: the initial state
-    # Checkpoints change nothing else, in either form.
     o2, s2, _ = run_gpu(x, **kw)
-    assert np.array_equal(o, o2) and np.array_equal(s, s2)
+    if kw.get("segment_chunks", 0) > 0:
+        # Segmented: without checkpoints the call takes the affine-output form, which
+        # rounds differently from the re-run form that checkpoints need.
+        assert rel_err(o2, o_ref) <= TOL and rel_err(s2, s_ref) <= TOL
+    else:
+        # Serial form: checkpoints change nothing else.
+        assert np.array_equal(o, o2) and np.array_equal(s, s2)
     return ck
 
 

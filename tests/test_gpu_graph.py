@@ -35,23 +35,20 @@ def captured_equals_eager(x, name, **kw):
     st_in = d.pop("state_in")
     o = torch.empty_like(v)
     st = torch.empty((x.N, x.H, 128, 128), dtype=d["state_dtype"], device="cuda")
+    args = kda.make_args(B=x.B, T=x.T, H=x.H, N=x.N, cu_seqlens=d.get("cu_seqlens"),
+                         segment_chunks=kw.get("segment_chunks", 0),
+                         checkpoint_every=kw.get("checkpoint_every", 0))
+    ws = torch.empty(max(1, kda.kda_prefill_workspace_bytes(args)), dtype=torch.uint8,
+                     device="cuda")
     extra = dict(kw)
-    rows = 0
     if kw.get("checkpoint_every"):
         every = kw["checkpoint_every"]
         cu = np.asarray(x.cu_seqlens) if x.cu_seqlens is not None else np.arange(x.B + 1) * x.T
         counts = [(int(b - a) + every - 1) // every for a, b in zip(cu[:-1], cu[1:])]
         starts = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
-        rows = int(starts[-1])
         extra["checkpoint_cu_starts"] = torch.from_numpy(starts).cuda()
-        extra["state_checkpoints"] = torch.empty((rows, x.H, 128, 128),
+        extra["state_checkpoints"] = torch.empty((int(starts[-1]), x.H, 128, 128),
                                                  dtype=d["state_dtype"], device="cuda")
-    # the workspace size depends on the checkpoint row count (segmented form)
-    args = kda.make_args(B=x.B, T=x.T, H=x.H, N=x.N, cu_seqlens=d.get("cu_seqlens"),
-                         segment_chunks=kw.get("segment_chunks", 0),
-                         checkpoint_every=kw.get("checkpoint_every", 0), checkpoint_rows=rows)
-    ws = torch.empty(max(1, kda.kda_prefill_workspace_bytes(args)), dtype=torch.uint8,
-                     device="cuda")
     run = lambda: kda.kda_prefill(q, k, v, g, beta, st_in, o=o, state_out=st, workspace=ws,
                                   **d, **extra)
     run()
