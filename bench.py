@@ -119,7 +119,10 @@ def make_call(x, device, **extra):
     d = to_device(x, device)
     o = torch.empty_like(d["v"])
     st = torch.empty((x.N, x.H, D, D), dtype=d["state_dtype"], device=device)
-    args = kda.make_args(B=x.B, T=x.T, H=x.H, N=x.N, cu_seqlens=d.get("cu_seqlens"), **extra)
+    sized = dict(extra)
+    if extra.get("state_checkpoints") is not None:  # the size query sees the call's rows
+        sized["checkpoint_rows"] = extra["state_checkpoints"].shape[0]
+    args = kda.make_args(B=x.B, T=x.T, H=x.H, N=x.N, cu_seqlens=d.get("cu_seqlens"), **sized)
     ws = torch.empty(kda.kda_prefill_workspace_bytes(args), dtype=torch.uint8, device=device)
 
     def call(trace=None):
