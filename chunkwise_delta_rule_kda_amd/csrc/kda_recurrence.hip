@@ -821,16 +821,24 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
         xbase + (parity * 4 + w) * 1024 + lane * 16);
   };
 
+  // In the affine-output form the scan-output launch reads each start state S_p
+  // (p = 1 .. P-1) as BF16 operands: the packed blocks 2 w, 2 w + 1 of a wave go over the
+  // first of its two FP32 fragments in slot p, bytes this wave alone has read.
+  auto put_packed = [&](float* slot, bf16x8 v) {
+    *reinterpret_cast<bf16x8*>(slot + koff0) = v;
+  };
   f32x4 st[2];
   {
-    const float* s1 = sbase + 1 * (kD * kD);
+    float* s1 = sbase + 1 * (kD * kD);
     st[0] = load4<false>(s1, koff0);
     st[1] = load4<false>(s1, koff1);
+    const bf16x8 v = pack8(st[0], st[1]);
+    *xch(1, wave) = v;  // S_1, read by step 1
+    if (p.affine_out) put_packed(s1, v);
   }
   CombineIn in[kCombineDepth];
 #pragma unroll
   for (int d = 0; d < kCombineDepth; ++d) fetch(in[d], 1 + d);
-  *xch(1, wave) = pack8(st[0], st[1]);  // S_1, read by step 1
   lds_barrier();
 
   // Step s: S_{s+1} = S_s Phi_s + Z_s with operands in set (s - 1) % depth; the set is
@@ -850,11 +858,16 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
         acc = mfma32(__builtin_bit_cast(bf16x8, in[set].a[i][kk]), sp[kk], acc);
       st[i] = acc + in[set].z[i];
     }
-    *xch((s + 1) & 1, wave) = pack8(st[0], st[1]);
+    const bf16x8 v = pack8(st[0], st[1]);
+    *xch((s + 1) & 1, wave) = v;
     if (s + 1 < nseg) {
       float* out = sbase + (s + 1) * (kD * kD);  // S_{s+1} replaces Z_s
-      store4<false>(out, koff0, st[0]);
-      store4<false>(out, koff1, st[1]);
+      if (p.affine_out) {
+        put_packed(out, v);
+      } else {
+        store4<false>(out, koff0, st[0]);
+        store4<false>(out, koff1, st[1]);
+      }
     } else if (p.state_out && srow >= 0) {  // S_P: the final state
       store4<BF16ST>(p.state_out, srow + 16 * (2 * wave) + 4 * (lane >> 4), st[0]);
       store4<BF16ST>(p.state_out, srow + 16 * (2 * wave + 1) + 4 * (lane >> 4), st[1]);
@@ -878,10 +891,11 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
 // (into o and scan_q). Every chunk of segments 1 .. P-1 is then independent: this
 // launch adds the second term to o, kScanOutChunks chunks of one segment per
 // workgroup, wave w for values 32 w .. 32 w + 31 (row blocks 2 w, 2 w + 1). Per chunk a
-// wave runs eight 16x16x32 products with S_p (packed once) as the A operand and the
-// chunk's Qt Phi^T fragments (four contiguous 1 KB pieces) as the B operand. The
-// launch moves little data (the o term is read and written once, Qt Phi^T read once),
-// so it is bound by load latency: small workgroups, all resident in one round.
+// wave runs eight 16x16x32 products with S_p (BF16, packed by the combine) as the A
+// operand and the chunk's Qt Phi^T fragments (four contiguous 1 KB pieces) as the B
+// operand. The launch moves little data (the o term is read and written once, Qt Phi^T
+// read once), so it is bound by load latency: small workgroups, all resident in one
+// round.
 struct ScanOutIn {
   bf16x8 q[4];  // Qt Phi^T fragments of the chunk
   f32x4 oz[2];  // O^Z[token m][values 16 rb + 4 grp + j], rb = 2 w + i
@@ -946,14 +960,16 @@ __global__ __launch_bounds__(256, BF16IO ? 3 : 2) void kda_scan_output_kernel(Pa
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int m = lane & 15;
   const int grp = lane >> 4;
-  // S_p rows 16 rb + m, packed as the recurrence packs its state (keys in the 16x16x32
-  // operand order).
+  // S_p rows 16 rb + m, packed by the combine as the recurrence packs its state (keys in
+  // the 16x16x32 operand order): key group kb of row block rb sits where the FP32
+  // fragment of key block 2 kb was.
   const float* sp_src = p.scan_s + (h * p.seg_stride + first + seg) * (kD * kD);
-  f32x4 sp_f[2][8];
+  bf16x8 sa[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) sp_f[i][b] = load4<false>(sp_src, state_frag(2 * wave + i, b, lane));
+    for (int kb = 0; kb < 4; ++kb)
+      sa[i][kb] = *reinterpret_cast<const bf16x8*>(sp_src + state_frag(2 * wave + i, 2 * kb, lane));
 
   const int64_t vstride = H * kD;
   const int64_t qbase = (h * p.max_chunks + chunk0) * (4 * 64 * 8) + lane * 8;
@@ -973,12 +989,6 @@ __global__ __launch_bounds__(256, BF16IO ? 3 : 2) void kda_scan_output_kernel(Pa
       in[j].oz[1] = load4<BF16IO>(p.o, obase + c * kC * vstride + 16);
     }
   }
-  bf16x8 sa[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      sa[i][kb] = pack8(sp_f[i][2 * kb], sp_f[i][2 * kb + 1]);
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < kScanOutChunks; ++j) {

@@ -219,6 +219,10 @@ typedef struct kda_prefill_args {
  *                                 segment, S = segments_per_head_bound; inside a slot,
  *                                 MFMA fragments [row block 8][key block 8][lane 64][4]
  *                                 with lane 16 g + m holding S[16 rb + m][16 b + 4 g + j].
+ *                                 In the affine-output form the combine then packs
+ *                                 each later segment's start state to BF16 in place:
+ *                                 blocks 2 kb and 2 kb + 1 as eight BF16 per lane over
+ *                                 the FP32 fragment of block 2 kb.
  *   scan_transition_offset        segmented form only: BF16 [H][S] slots of 128 x 128,
  *                                 each later segment's transition Phi, as fragments
  *                                 [key block 8][key group 4][lane 64][8] with lane
