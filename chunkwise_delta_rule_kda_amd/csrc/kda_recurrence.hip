@@ -43,18 +43,20 @@
 //
 // Workgroup. W compute waves (16 value rows each, W = 1, 2, 4) plus NL loader waves.
 // The loaders stream each chunk's record and V tile with 16-byte loads, DEPTH chunks
-// ahead in registers, into a 3-slot LDS ring; one s_barrier per chunk publishes a slot.
-// (One workgroup streams at most ~60 GB/s; two loader waves with three or more chunks
-// in flight reach that, one wave or one chunk in flight does not, and LDS-DMA loads
-// deliver only ~16 B/clock.) Compute waves touch LDS and registers only.
+// ahead in registers, into a 4-slot LDS ring; one s_barrier per chunk publishes a slot.
+// (LDS-DMA loads deliver only ~16 B/clock.) Compute waves touch LDS and registers only.
 //
 // Ring protocol, iteration c:
-//   loaders: write chunk c+1 into slot (c+1)%3, issue the loads of chunk c+1+DEPTH,
-//            wait for their own LDS writes, barrier B_c;
-//   compute: barrier B_c, read all of chunk c+1's operands (slot (c+1)%3), compute c
+//   loaders: issue the loads of chunk c+1+DEPTH, write chunk c+2 into slot (c+2)%4,
+//            wait for their own LDS writes of chunk c+1 (issued in iteration c-1),
+//            barrier B_c;
+//   compute: barrier B_c, read all of chunk c+1's operands (slot (c+1)%4), compute c
 //            (operands read in the previous iteration), store the O of chunk c-1.
-// Slot (c+1)%3 last held chunk c-2, whose reads were consumed before B_{c-2}; the
-// loaders write it after B_{c-1}.
+// A chunk is written one iteration before the barrier that publishes it, so no wave
+// waits for LDS writes it has just issued, and the global loads go out before the LDS
+// writes, which queue behind the compute waves' reads (measured: a loader that wrote,
+// waited for its writes, then issued its loads set the chunk time). Slot (c+2)%4 last held chunk c-2, whose reads were consumed before
+// B_{c-1}; the loaders write it after B_{c-1}.
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -63,7 +65,7 @@ namespace kda {
 
 namespace {
 
-constexpr int kSlots = 3;
+constexpr int kSlots = 4;
 constexpr int kRecUnits = kRecord / 16;  // 864 sixteen-byte units per record
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -79,9 +81,10 @@ __device__ __forceinline__ void lds_barrier() {
   compiler_fence();
 }
 
-// Meet the other waves without waiting for this wave's own LDS reads (a wave that only
-// reads LDS: every read it issues is consumed, and so complete, before the wave reaches
-// the barrier after next, the first after which that slot is rewritten).
+// Meet the other waves without waiting for this wave's own LDS operations. A compute
+// wave's reads are consumed, and so complete, before it reaches the barrier after next
+// (the first after which their slot is rewritten); a loader waits for its writes at
+// the start of its next iteration, before the barrier that publishes them.
 __device__ __forceinline__ void read_barrier() {
   compiler_fence();
   __builtin_amdgcn_s_barrier();
@@ -119,7 +122,7 @@ struct Tile {
   static constexpr int SLOT = K * LT * 16;                // padded ring slot
   static_assert(K * (DEPTH - 1) <= 63, "vmcnt range");
   static_assert(DEPTH >= 2, "loader pipeline");
-  static_assert(kSlots * SLOT <= 65536, "LDS ring");
+  static_assert(kSlots * SLOT <= 81920, "LDS ring");  // of gfx950's 160 KB per CU
 };
 
 // Scan slots hold MFMA fragments, so that every access to them is one contiguous 1 KB
@@ -487,11 +490,33 @@ __device__ __forceinline__ f32x4 chunk_step(const ChainIn& a, const TailIn& b, f
 // tail). Chunks past the run's end re-read its last chunk (in bounds, never used).
 // OUT false: the record units that hold Qt (whole iterations k of the unit loop, for both
 // loader widths) are neither loaded nor written.
+// Loader units k of a chunk that a run without O skips (the Qt tile), and the number of
+// LDS writes one loader wave issues per chunk.
+template <typename T, bool OUT>
+constexpr bool unit_skipped(int k) {
+  return !OUT && k * T::LT >= kOffQt / 16 && (k + 1) * T::LT <= (kOffQt + 4096) / 16;
+}
+template <typename T, bool OUT>
+constexpr int writes_per_chunk() {
+  int n = 0;
+  for (int k = 0; k < T::K; ++k) n += unit_skipped<T, OUT>(k) ? 0 : 1;
+  return n;
+}
+
+// Wait until at most N of this wave's LDS operations are outstanding: as they complete
+// in order, all but its N most recent ones are done.
+template <int N>
+__device__ __forceinline__ void lds_wait_n() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xc07f | (N << 8));  // lgkmcnt(N)
+  compiler_fence();
+}
+
 template <bool BF16IO, typename T, bool OUT>
 __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_u8* ring, int lt) {
-  auto skipped = [](int k) {
-    return !OUT && k * T::LT >= kOffQt / 16 && (k + 1) * T::LT <= (kOffQt + 4096) / 16;
-  };
+  auto skipped = [](int k) { return unit_skipped<T, OUT>(k); };
+  constexpr int KW = writes_per_chunk<T, OUT>();
   const int64_t vstride_b = p.H * kD * T::ES;
   const unsigned char* rec0 =
       p.records + (t.h * p.max_chunks + t.rec_chunk) * static_cast<int64_t>(kRecord);
@@ -523,7 +548,11 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
       inc[k] = kRecord;
     }
   }
-  u32x4 r[T::DEPTH][T::K];
+  // Chunk j lives in register set j % NS: one set more than the DEPTH chunks in flight,
+  // so that the set reloaded in an iteration held a chunk whose LDS writes were complete
+  // before the previous barrier.
+  constexpr int NS = T::DEPTH + 1;
+  u32x4 r[NS][T::K];
   auto issue = [&](u32x4(&dst)[T::K], int64_t j) {
     j = j < nch - 1 ? j : nch - 1;
     const int64_t nvalid = t.tok_end - (t.tok0 + j * kC);
@@ -542,40 +571,56 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
       }
     }
   };
+  // One ds_write_b128 per unit, written out as such, so that the wave's LDS operations
+  // per chunk are exactly KW writes (the wait before each barrier counts them).
+  const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
   auto put = [&](const u32x4(&src)[T::K], int slot) {
-    lds_u8* s = ring + slot * T::SLOT;
+    const uint32_t s = ring_addr + static_cast<uint32_t>(slot * T::SLOT + lt * 16);
 #pragma unroll
     for (int k = 0; k < T::K; ++k) {
       if (skipped(k)) continue;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(s + (lt + k * T::LT) * 16) =
-          src[k];
+      asm volatile("ds_write_b128 %0, %1" ::"v"(s + static_cast<uint32_t>(k * T::LT * 16)),
+                   "v"(src[k])
+                   : "memory");
     }
   };
 #pragma unroll
   for (int d = 0; d < T::DEPTH; ++d) issue(r[d], d);
   put(r[0], 0);
-  issue(r[0], T::DEPTH);
-  lds_barrier();  // B_{-1}: chunk 0 visible
-  int slot = 0;  // slot of chunk c
-  // Iteration c: chunk c + 1 (register set (c + 1) % DEPTH) into the ring, chunk
-  // c + 1 + DEPTH into that set, barrier B_c. Whole groups of DEPTH iterations are
-  // unrolled without conditions so that the compiler's wait before each LDS write is
-  // for the oldest set only (DEPTH - 1 chunks stay in flight).
-  auto step = [&](auto set_c, int64_t c) {
-    constexpr int set = decltype(set_c)::value;
-    slot = slot + 1 == kSlots ? 0 : slot + 1;  // slot of chunk c + 1
-    put(r[set], slot);
-    issue(r[set], c + 1 + T::DEPTH);
-    lds_barrier();  // B_c
+  issue(r[T::DEPTH], T::DEPTH);  // the spare set
+  put(r[1], 1);
+  lds_barrier();  // B_{-1}: chunk 0 visible (chunk 1 written too)
+  int slot = 1;  // slot of chunk c + 1
+  // Iteration c: the set of chunk c (its writes, iteration c - 2, were complete before
+  // B_{c-1}) is reloaded with chunk c + 1 + DEPTH, chunk c + 2 goes into the ring, and
+  // once this wave's writes of chunk c + 1 (iteration c - 1) are done, barrier B_c
+  // publishes chunk c + 1. No wave waits for the LDS writes it has just issued, which
+  // queue behind the compute waves' reads of chunk c + 1, and the global loads go out
+  // first (measured: a loader that wrote, waited for those writes, then issued its
+  // loads set the chunk time). Whole groups of NS iterations are unrolled without
+  // conditions so that the compiler's wait before each LDS write is for the oldest set
+  // only (DEPTH - 1 chunks stay in flight). Chunks past the run's last are clamped reads
+  // of it, written and never read.
+  auto step = [&](auto load_c, auto put_c, int64_t c) {
+    constexpr int lset = decltype(load_c)::value;  // set of chunk c
+    constexpr int pset = decltype(put_c)::value;   // set of chunk c + 2
+    issue(r[lset], c + 1 + T::DEPTH);
+    slot = slot + 1 == kSlots ? 0 : slot + 1;  // slot of chunk c + 2
+    put(r[pset], slot);
+    lds_wait_n<KW>();  // all but the writes just issued
+    read_barrier();    // B_c: chunk c + 1 visible; chunk c + 2 at B_{c+1}
   };
   int64_t c0 = 0;
 #pragma unroll 1
-  for (; c0 + T::DEPTH <= nch; c0 += T::DEPTH)
-    unroll<T::DEPTH>([&](auto d) { step(IntC<(decltype(d)::value + 1) % T::DEPTH>{}, c0 + decltype(d)::value); });
-  const int64_t rest = nch - c0;  // 0 .. DEPTH - 1
-  unroll<T::DEPTH - 1>([&](auto d) {
+  for (; c0 + NS <= nch; c0 += NS)
+    unroll<NS>([&](auto d) {
+      constexpr int i = decltype(d)::value;
+      step(IntC<i>{}, IntC<(i + 2) % NS>{}, c0 + i);
+    });
+  const int64_t rest = nch - c0;  // 0 .. NS - 1
+  unroll<NS - 1>([&](auto d) {
     constexpr int i = decltype(d)::value;
-    if (rest > i) step(IntC<(i + 1) % T::DEPTH>{}, c0 + i);
+    if (rest > i) step(IntC<i>{}, IntC<(i + 2) % NS>{}, c0 + i);
   });
 }
 
@@ -705,11 +750,12 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
     // key 16 b + m' (m' = 4 grp + j) sits in group kk = r / 32, lane 16 grp' + m',
     // element e with r % 32 = 16 (e / 4) + 4 grp' + e % 4. This wave's 16 rows fill
     // elements 4 h .. 4 h + 3 (h = v0 / 16 % 2) of every (b, lane) piece of group kk: the
-    // values go through this wave's 4 KB of ring slot (nch + 1) % 3 ([b 8][lane 64][4]),
-    // then out as one 8-byte store per lane and b. Every wave has finished with that slot
-    // once past barrier B_{nch-1} (its last reads were consumed in iteration nch - 2);
-    // an empty run never touched the ring.
-    lds_u8* stage = ring + ((nch + 1) % kSlots) * T::SLOT + wave * 4096;
+    // values go through this wave's 4 KB of ring slot nch % 4 ([b 8][lane 64][4]), then
+    // out as one 8-byte store per lane and b. The loaders last wrote that slot with
+    // chunk nch (a clamped copy) and waited for those writes before barrier B_{nch-1};
+    // the compute waves only read it after that barrier (chunk nch, values unused, in
+    // this wave's own order before these writes). An empty run never touched the ring.
+    lds_u8* stage = ring + (nch % kSlots) * T::SLOT + wave * 4096;
     const int r = v0 + m;
     const int kk = r >> 5;
     const int h = (r >> 4) & 1;
