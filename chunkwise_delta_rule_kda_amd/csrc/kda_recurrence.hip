@@ -525,8 +525,9 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
                             (t.tok0 * p.H * kD + t.h * kD + vcol) * T::ES;
   const int64_t vchunk_b = kC * vstride_b;
   const int64_t nch = t.nch;
-  // Per-unit source address of chunk 0 and its step per chunk. A V unit of a pad token
-  // (past the sequence end, only in a sequence's last chunk) reads token row 0 instead.
+  // Per-unit source address of chunk 0 (then of the next chunk to load) and its step per
+  // chunk. A V unit of a pad token (past the sequence end, only in a sequence's last
+  // chunk) reads token row 0 instead.
   const unsigned char* base[T::K];
   uint32_t inc[T::K];
   int vtok[T::K];       // V token row of the unit, or -1 for a record unit
@@ -553,23 +554,30 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
   // before the previous barrier.
   constexpr int NS = T::DEPTH + 1;
   u32x4 r[NS][T::K];
-  auto issue = [&](u32x4(&dst)[T::K], int64_t j) {
-    j = j < nch - 1 ? j : nch - 1;
+  // Chunks are loaded in order, 0, 1, 2, ...: each unit keeps a running source pointer,
+  // which stops at the run's last chunk (later loads re-read it, never used).
+  int64_t jn = 0;  // the next chunk to load
+  auto issue = [&](u32x4(&dst)[T::K]) {
+    const int64_t j = jn < nch - 1 ? jn : nch - 1;
     const int64_t nvalid = t.tok_end - (t.tok0 + j * kC);
     if (nvalid >= kC) {
 #pragma unroll
       for (int k = 0; k < T::K; ++k)
-        if (!skipped(k))
-          dst[k] = *reinterpret_cast<const u32x4*>(base[k] + static_cast<uint64_t>(j) * inc[k]);
+        if (!skipped(k)) dst[k] = *reinterpret_cast<const u32x4*>(base[k]);
     } else {
 #pragma unroll
       for (int k = 0; k < T::K; ++k) {
         if (skipped(k)) continue;
-        const unsigned char* src = base[k] + static_cast<uint64_t>(j) * inc[k];
+        const unsigned char* src = base[k];
         if (vtok[k] >= nvalid) src -= vdrop[k];
         dst[k] = *reinterpret_cast<const u32x4*>(src);
       }
     }
+    if (jn < nch - 1) {
+#pragma unroll
+      for (int k = 0; k < T::K; ++k) base[k] += inc[k];
+    }
+    ++jn;
   };
   // One ds_write_b128 per unit, written out as such, so that the wave's LDS operations
   // per chunk are exactly KW writes (the wait before each barrier counts them).
@@ -585,9 +593,9 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
     }
   };
 #pragma unroll
-  for (int d = 0; d < T::DEPTH; ++d) issue(r[d], d);
+  for (int d = 0; d < T::DEPTH; ++d) issue(r[d]);  // chunks 0 .. DEPTH - 1
   put(r[0], 0);
-  issue(r[T::DEPTH], T::DEPTH);  // the spare set
+  issue(r[T::DEPTH]);  // chunk DEPTH, into the spare set
   put(r[1], 1);
   lds_barrier();  // B_{-1}: chunk 0 visible (chunk 1 written too)
   int slot = 1;  // slot of chunk c + 1
@@ -604,7 +612,7 @@ __device__ __forceinline__ void loader_loop(const Params& p, const Task& t, lds_
   auto step = [&](auto load_c, auto put_c, int64_t c) {
     constexpr int lset = decltype(load_c)::value;  // set of chunk c
     constexpr int pset = decltype(put_c)::value;   // set of chunk c + 2
-    issue(r[lset], c + 1 + T::DEPTH);
+    issue(r[lset]);  // chunk c + 1 + DEPTH
     slot = slot + 1 == kSlots ? 0 : slot + 1;  // slot of chunk c + 2
     put(r[pset], slot);
     lds_wait_n<KW>();  // all but the writes just issued
