@@ -86,7 +86,8 @@ kda_status check_shape(const kda_prefill_args* a) {
   if (!std::isfinite(a->scale) || a->scale < 0.0f)
     return fail(KDA_ERR_BOUND, "scale %g", (double)a->scale);
   if (a->rows_per_workgroup != 0 && a->rows_per_workgroup != 16 &&
-      a->rows_per_workgroup != 32 && a->rows_per_workgroup != 64)
+      a->rows_per_workgroup != 32 && a->rows_per_workgroup != 64 &&
+      a->rows_per_workgroup != 128)
     return fail(KDA_ERR_CONFIG, "rows_per_workgroup %d", a->rows_per_workgroup);
   if (a->segment_chunks > (1 << 24))
     return fail(KDA_ERR_CONFIG, "segment_chunks %d", a->segment_chunks);
@@ -151,6 +152,18 @@ bool decode_form(const kda_prefill_args* a) {
          a->checkpoint_every == 0 && a->rows_per_workgroup == 0 && a->segment_chunks == 0;
 }
 
+// Rows per workgroup of the segmented form: the explicit choice, else 64, or a whole
+// head's 128 rows (eight compute waves, BF16 I/O) past 32 (sequence, head) pairs,
+// where 64-row segments no longer fit. A chunk takes ~1 us in a 128-row workgroup
+// under full load against ~0.55 us in a 64-row one, but a segment needs half the
+// workgroups: measured on T = 8192, H = 48 segments of 128 rows beat the serial form
+// (419 vs 432 us), while H = 6 loses with them (79.5 vs 73.5 us: the combine and the
+// scan output grow with the segment count).
+int segmented_rows(const kda_prefill_args* a) {
+  if (a->rows_per_workgroup) return a->rows_per_workgroup;
+  return a->io_dtype == KDA_BF16 && a->N * a->H * 8 > kScanTargetCUs ? 128 : 64;
+}
+
 Plan make_plan(const kda_prefill_args* a) {
   Plan pl;
   pl.max_chunks = max_chunks_of(a);
@@ -162,13 +175,15 @@ Plan make_plan(const kda_prefill_args* a) {
     L = a->segment_chunks;
   } else if (a->segment_chunks == 0) {
     // Time segments pay off when few (sequence, head) pairs leave compute units idle:
-    // launch A has 4 P - 2 (affine-output form) or 4 P - 6 (with checkpoints)
-    // workgroups of 64 rows per pair for P segments; aim for one per compute unit,
-    // with segments of at least 16 chunks.
+    // with b = 128 / rows workgroups per 128 rows, launch A has b (2 P - 1)
+    // (affine-output form) or b (2 P - 3) (with checkpoints) workgroups per pair for P
+    // segments; aim for one per compute unit, with segments of at least 16 chunks, and
+    // take three segments or more (two when at most 32 pairs).
     const int64_t pairs = a->N * a->H;
-    if (pairs > 0 && pairs * 8 <= kScanTargetCUs) {
-      const int64_t P = (kScanTargetCUs / pairs + (a->checkpoint_every > 0 ? 6 : 2)) / 4;
-      if (P >= 2) {
+    if (pairs > 0) {
+      const int64_t b = kda::kD / segmented_rows(a);
+      const int64_t P = (kScanTargetCUs / (pairs * b) + (a->checkpoint_every > 0 ? 3 : 1)) / 2;
+      if (P >= 3 || (P >= 2 && pairs * 8 <= kScanTargetCUs)) {
         L = (per_seq + P - 1) / P;
         if (L < 16) L = 16;
       }
@@ -242,12 +257,12 @@ int64_t scan_c_workgroups(const kda_prefill_args* a, const Plan& pl, int rows) {
   return a->H * a->N * (pl.segs_per_seq - 1) * b0;
 }
 
-// Rows per workgroup of the recurrence launches: the explicit choice, else 64 in the
-// segmented form (launch A alone has about one workgroup per compute unit) and the
+// Rows per workgroup of the recurrence launches: the explicit choice, else the
+// segmented form's (launch A alone has about one workgroup per compute unit) and the
 // fill rule in the serial form.
 int rows_of(const kda_prefill_args* a, const Plan& pl, int num_cus) {
   if (a->rows_per_workgroup) return a->rows_per_workgroup;
-  return pl.seg_len > 0 ? 64 : rows_per_wg(a, num_cus);
+  return pl.seg_len > 0 ? segmented_rows(a) : rows_per_wg(a, num_cus);
 }
 
 std::atomic<int> g_cu_count[64];

@@ -41,7 +41,7 @@
 // run), rows 128..255 the rows of Phi. Serial mode (one segment per sequence) is the
 // single launch of the plain recurrence.
 //
-// Workgroup. W compute waves (16 value rows each, W = 1, 2, 4) plus NL loader waves.
+// Workgroup. W compute waves (16 value rows each, W = 1, 2, 4, 8) plus NL loader waves.
 // The loaders stream each chunk's record and V tile with 16-byte loads, DEPTH chunks
 // ahead in registers, into a 4-slot LDS ring; one s_barrier per chunk publishes a slot.
 // (LDS-DMA loads deliver only ~16 B/clock.) Compute waves touch LDS and registers only.
@@ -122,7 +122,7 @@ struct Tile {
   static constexpr int SLOT = K * LT * 16;                // padded ring slot
   static_assert(K * (DEPTH - 1) <= 63, "vmcnt range");
   static_assert(DEPTH >= 2, "loader pipeline");
-  static_assert(kSlots * SLOT <= 81920, "LDS ring");  // of gfx950's 160 KB per CU
+  static_assert(kSlots * SLOT <= 98304, "LDS ring");  // of gfx950's 160 KB per CU
 };
 
 // Scan slots hold MFMA fragments, so that every access to them is one contiguous 1 KB
@@ -758,28 +758,34 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
     // key 16 b + m' (m' = 4 grp + j) sits in group kk = r / 32, lane 16 grp' + m',
     // element e with r % 32 = 16 (e / 4) + 4 grp' + e % 4. This wave's 16 rows fill
     // elements 4 h .. 4 h + 3 (h = v0 / 16 % 2) of every (b, lane) piece of group kk: the
-    // values go through this wave's 4 KB of ring slot nch % 4 ([b 8][lane 64][4]), then
-    // out as one 8-byte store per lane and b. The loaders last wrote that slot with
-    // chunk nch (a clamped copy) and waited for those writes before barrier B_{nch-1};
-    // the compute waves only read it after that barrier (chunk nch, values unused, in
-    // this wave's own order before these writes). An empty run never touched the ring.
-    lds_u8* stage = ring + (nch % kSlots) * T::SLOT + wave * 4096;
+    // values go through this wave's 2 KB of ring slot nch % 4 ([b 4][lane 64][4]), in two
+    // halves of four key blocks, then out as one 8-byte store per lane and b. The
+    // loaders last wrote that slot with chunk nch (a clamped copy) and waited for those
+    // writes before barrier B_{nch-1}; the compute waves only read it after that barrier
+    // (chunk nch, values unused, in this wave's own order before these writes). An empty
+    // run never touched the ring.
+    static_assert(W * 2048 <= T::SLOT, "Phi staging");
+    lds_u8* stage = ring + (nch % kSlots) * T::SLOT + wave * 2048;
     const int r = v0 + m;
     const int kk = r >> 5;
     const int h = (r >> 4) & 1;
     const int grpp = (r & 15) >> 2;
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<__attribute__((address_space(3))) unsigned short*>(
-            stage + ((b * 64 + 16 * grpp + 4 * grp + j) * 4 + (r & 3)) * 2) =
-            float_to_bf16_bits(st[b][j]);
+      for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const u32x2 piece =
-          *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(stage + (b * 64 + lane) * 8);
-      *reinterpret_cast<u32x2*>(t.phi_dst + ((b * 4 + kk) * 64 + lane) * 8 + 4 * h) = piece;
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<__attribute__((address_space(3))) unsigned short*>(
+              stage + ((bb * 64 + 16 * grpp + 4 * grp + j) * 4 + (r & 3)) * 2) =
+              float_to_bf16_bits(st[4 * half + bb][j]);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int b = 4 * half + bb;
+        const u32x2 piece = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+            stage + (bb * 64 + lane) * 8);
+        *reinterpret_cast<u32x2*>(t.phi_dst + ((b * 4 + kk) * 64 + lane) * 8 + 4 * h) = piece;
+      }
     }
   }
 }
@@ -789,7 +795,8 @@ __device__ __forceinline__ void compute_loop(const Params& p, const Task& t, lds
 template <bool BF16IO, bool BF16ST, int W, bool CK>
 // At most two waves per SIMD (256 registers each): with more room the compiler keeps
 // the state in AGPRs and copies it through VGPRs every chunk for the decay multiply.
-__global__ __launch_bounds__(block_threads(W), 2) void kda_recurrence_kernel(Params p) {
+// The 128-row workgroup (12 waves) needs three waves per SIMD, 168 registers each.
+__global__ __launch_bounds__(block_threads(W), W == 8 ? 3 : 2) void kda_recurrence_kernel(Params p) {
   using T = Tile<BF16IO, W>;
   static_assert(T::NT == block_threads(W), "block size");
   __shared__ __attribute__((aligned(16))) unsigned char ring_[kSlots * T::SLOT];
@@ -1070,9 +1077,13 @@ void launch_waves(const Params& p, dim3 grid, hipStream_t stream) {
       hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 2, CK>), grid,
                          dim3(Tile<BF16IO, 2>::NT), 0, stream, p);
       break;
-    default:
+    case 4:
       hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 4, CK>), grid,
                          dim3(Tile<BF16IO, 4>::NT), 0, stream, p);
+      break;
+    default:
+      hipLaunchKernelGGL((kda_recurrence_kernel<BF16IO, BF16ST, 8, CK>), grid,
+                         dim3(Tile<BF16IO, 8>::NT), 0, stream, p);
       break;
   }
 }
@@ -1090,7 +1101,7 @@ int recurrence_loader_waves(int compute_waves) { return loader_waves(compute_wav
 hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16, bool state_bf16,
                              hipStream_t stream) {
   if (workgroups <= 0) return hipSuccess;
-  if (p.waves != 1 && p.waves != 2 && p.waves != 4) return hipErrorInvalidValue;
+  if (p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != 8) return hipErrorInvalidValue;
   workgroups = (workgroups + 7) / 8 * 8;  // whole XCD rounds (see task_index)
   if (workgroups > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(workgroups));

@@ -71,7 +71,7 @@ typedef enum kda_status {
   KDA_ERR_WORKSPACE = 7,  /* workspace NULL, too small or not 256-byte aligned */
   KDA_ERR_HIP = 8,        /* a HIP runtime call or kernel launch failed */
   KDA_ERR_CU_SEQLENS = 9, /* kda_debug_check_cu_seqlens found a contract violation */
-  KDA_ERR_CONFIG = 10     /* rows_per_workgroup not 0, 16, 32 or 64, segment_chunks
+  KDA_ERR_CONFIG = 10     /* rows_per_workgroup not 0, 16, 32, 64 or 128, segment_chunks
                              above 2^24, checkpoint_every not a multiple of 16 (or
                              negative), checkpoint_rows negative, or a state pool
                              with no slots, a pitch below H * 128 * 128 or not a
@@ -124,7 +124,7 @@ typedef struct kda_prefill_args {
   uint32_t flags;        /* KDA_FLAG_* */
 
   /* Launch geometry: value rows handled by one workgroup of the recurrence (each
-     compute wave owns 16 rows). 0 = automatic; 16/32/64 force it. For a given
+     compute wave owns 16 rows). 0 = automatic; 16/32/64/128 force it. For a given
      segment_chunks, results are bitwise identical for every choice. */
   int32_t rows_per_workgroup;
 
@@ -140,10 +140,12 @@ typedef struct kda_prefill_args {
      is instead re-run from its true start (the states inside it are needed): about two
      segments. Either way about twice or three times the recurrence work buys the
      shorter path, which pays off when few (sequence, head) pairs leave compute units
-     idle. 0 = automatic (segments only when N * H <= 32, sized so the first pass has
-     about one workgroup per compute unit of a 256-CU device); negative = never (one
-     serial run per sequence); positive = this many chunks per segment. Results differ
-     from the serial form only by rounding. */
+     idle. 0 = automatic: P segments (of at least 16 chunks) such that the first pass
+     has about one workgroup per compute unit of a 256-CU device, with 64-row
+     workgroups (128-row ones for BF16 I/O past N * H = 32) unless rows_per_workgroup
+     says otherwise, taken when P >= 3, or P >= 2 with N * H <= 32; negative = never
+     (one serial run per sequence); positive = this many chunks per segment. Results
+     differ from the serial form only by rounding. */
   int32_t segment_chunks;
 
   /* State checkpoints, as in the "flashinfer.kda_prefill" page's contract (section

@@ -186,13 +186,15 @@ def test_plan_follows_the_slice_rule():
     assert p["prepare_workgroups"] == 512 * 96
     # serial grid: whole rounds of 8 (sequence, head) pairs, each with its row blocks
     assert kda.kda_prefill_plan(fake(H=6, rows_per_workgroup=64), 256)["recurrence_workgroups"] == 16
-    assert status(fake(rows_per_workgroup=128)) == 10
+    assert status(fake(rows_per_workgroup=128)) == 0
     assert status(fake(rows_per_workgroup=48)) == 10
+    assert status(fake(rows_per_workgroup=256)) == 10
 
 
 def test_plan_segments_small_head_counts():
-    # H = 6, T = 8192: 512 chunks. Affine-output form (no checkpoints): launch A has
-    # 4 P - 2 workgroups per pair, so P = (256 / 6 + 2) / 4 = 11 segments of 47 chunks.
+    # H = 6, T = 8192: 512 chunks. Affine-output form (no checkpoints), 64-row
+    # workgroups: launch A has 2 (2 P - 1) workgroups per pair, so
+    # P = (256 / 12 + 1) / 2 = 11 segments of 47 chunks.
     p = kda.kda_prefill_plan(fake(H=6, T=8192), 256)
     assert p["segment_chunks"] == 47 and p["segments_per_head_bound"] == 11
     assert p["rows_per_workgroup"] == 64 and p["scan_affine_output"] == 1
@@ -209,13 +211,26 @@ def test_plan_segments_small_head_counts():
     assert p["scan_output_offset"] == records + slots * 128 * 128 * 6
     need = kda.kda_prefill_workspace_bytes(fake(H=6, T=8192))
     assert need == records + slots * 128 * 128 * 6 + 512 * 6 * 2048 * 2
-    # With checkpoints every later segment is re-run: 4 P - 6 workgroups per pair in
-    # launch A, P = (256 / 6 + 6) / 4 = 12 segments of 43 chunks.
+    # With checkpoints every later segment is re-run: 2 (2 P - 3) workgroups per pair in
+    # launch A, P = (256 / 12 + 3) / 2 = 12 segments of 43 chunks.
     c = kda.kda_prefill_plan(fake(H=6, T=8192, checkpoint_every=1024), 256)
     assert c["segment_chunks"] == 43 and c["segments_per_head_bound"] == 12
     assert c["scan_affine_output"] == 0 and c["scan_output_offset"] == 0
     assert c["recurrence_workgroups"] == 6 * (2 + 4 * 10)
     assert c["scan_c_workgroups"] == 6 * 11 * 2
+    # 128-row workgroups when asked for: 2 P - 1 per pair, P = (256 / 6 + 1) / 2 = 21.
+    w = kda.kda_prefill_plan(fake(H=6, T=8192, rows_per_workgroup=128), 256)
+    assert w["segment_chunks"] == 25 and w["segments_per_head_bound"] == 21
+    assert w["rows_per_workgroup"] == 128 and w["waves_per_workgroup"] == 8 + 4
+    assert w["recurrence_workgroups"] == 6 * (1 + 2 * 20)
+    # Past 32 pairs (BF16 I/O) the automatic segments use 128-row workgroups and need
+    # three segments: H = 48 (P = 3) is segmented, H = 64 (P = 2) and H = 96 are not;
+    # with FP32 I/O H = 48 stays serial.
+    h48 = kda.kda_prefill_plan(fake(H=48, T=8192), 256)
+    assert h48["segment_chunks"] == 171 and h48["rows_per_workgroup"] == 128
+    assert h48["recurrence_workgroups"] == 48 * 5
+    assert kda.kda_prefill_plan(fake(H=64, T=8192), 256)["segment_chunks"] == 0
+    assert kda.kda_prefill_plan(fake(H=48, T=8192, io=kda.KDA_FP32), 256)["segment_chunks"] == 0
     # Forced serial, forced length, and no segments for many heads.
     s = kda.kda_prefill_plan(fake(H=6, T=8192, segment_chunks=-1), 256)
     assert s["segment_chunks"] == 0 and s["rows_per_workgroup"] == 16

@@ -85,7 +85,7 @@ def test_stress_gate_weak_varlen():
 def test_bitwise_identical_across_slices_and_runs():
     x = kda_synth.config(2, T=160, H=2)
     ref_o, ref_s, _ = run_gpu(x, rows_per_workgroup=16)
-    for rows in (16, 32, 64, 0):
+    for rows in (16, 32, 64, 128, 0):
         o, s, _ = run_gpu(x, rows_per_workgroup=rows)
         assert np.array_equal(o, ref_o) and np.array_equal(s, ref_s), rows
 

@@ -4,7 +4,7 @@ The loader waves stage chunks through a 4-slot LDS ring and keep their global lo
 register sets used in rotation, unrolled in whole groups of sets, with a remainder loop
 for the last chunks of a run. One varlen call whose sequences span every chunk count
 from 1 to 13 (ragged tails and whole chunks) exercises every remainder and every slot
-wrap-around, for each workgroup shape (16, 32 and 64 rows: different loader counts and
+wrap-around, for each workgroup shape (16, 32, 64 and 128 rows: different loader counts and
 set counts) in the serial form, with and without state checkpoints, and, with short
 segments, in the segmented form. The weak gate keeps the carry across chunks large,
 so a chunk staged in the wrong slot or read too early changes the result.
@@ -56,12 +56,12 @@ def test_lengths_cover_every_chunk_count():
     assert sorted((n + 15) // 16 for n in LENGTHS) == list(range(1, 14))
 
 
-@pytest.mark.parametrize("rows", [16, 32, 64])
+@pytest.mark.parametrize("rows", [16, 32, 64, 128])
 def test_serial_run_lengths(inputs, rows):
     check(inputs, f"serial rows={rows}", rows_per_workgroup=rows, segment_chunks=-1)
 
 
-@pytest.mark.parametrize("rows", [16, 64])
+@pytest.mark.parametrize("rows", [16, 64, 128])
 def test_serial_run_lengths_with_checkpoints(inputs, rows):
     check(inputs, f"serial rows={rows} checkpoints", rows_per_workgroup=rows,
           segment_chunks=-1, checkpoint_every=32)
