@@ -55,8 +55,11 @@
 // A chunk is written one iteration before the barrier that publishes it, so no wave
 // waits for LDS writes it has just issued, and the global loads go out before the LDS
 // writes, which queue behind the compute waves' reads (measured: a loader that wrote,
-// waited for its writes, then issued its loads set the chunk time). Slot (c+2)%4 last held chunk c-2, whose reads were consumed before
-// B_{c-1}; the loaders write it after B_{c-1}.
+// waited for its writes, then issued its loads set the chunk time). Slot (c+2)%4 last
+// held chunk c-2, whose reads were consumed before B_{c-1}; the loaders write it after
+// B_{c-1}.
+
+#include <type_traits>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -957,9 +960,13 @@ __global__ __launch_bounds__(256) void kda_combine_kernel(Params p) {
 // operand. The launch moves little data (the o term is read and written once, Qt Phi^T
 // read once), so it is bound by load latency: small workgroups, all resident in one
 // round.
+template <bool BF16IO>
 struct ScanOutIn {
   bf16x8 q[4];  // Qt Phi^T fragments of the chunk
-  f32x4 oz[2];  // O^Z[token m][values 16 rb + 4 grp + j], rb = 2 w + i
+  // O^Z[token m][values 16 rb + 4 grp + j], rb = 2 w + i, as loaded (BF16 pairs are
+  // widened when used: two registers per piece instead of four, so that four
+  // workgroups fit per CU)
+  typename std::conditional<BF16IO, u32x2, f32x4>::type oz[2];
 };
 
 template <bool BF16IO>
@@ -973,7 +980,7 @@ __device__ __forceinline__ bf16x8 load_frag(const void* base, int64_t idx) {
 }
 
 template <bool BF16IO>
-__global__ __launch_bounds__(256, BF16IO ? 3 : 2) void kda_scan_output_kernel(Params p) {
+__global__ __launch_bounds__(256, BF16IO ? 4 : 2) void kda_scan_output_kernel(Params p) {
   const int64_t groups = (p.seg_len + kScanOutChunks - 1) / kScanOutChunks;
   const int64_t task = task_index();  // consecutive tasks (one segment) share an XCD
   const int64_t H = p.H;
@@ -1038,7 +1045,7 @@ __global__ __launch_bounds__(256, BF16IO ? 3 : 2) void kda_scan_output_kernel(Pa
   // Every load of the workgroup is issued before the first product: the latency of one
   // round trip, not one per chunk, sets the time. Chunks past c1 re-read chunk c1 - 1
   // (in bounds, never stored).
-  ScanOutIn in[kScanOutChunks];
+  ScanOutIn<BF16IO> in[kScanOutChunks];
 #pragma unroll
   for (int j = 0; j < kScanOutChunks; ++j) {
     const int64_t c = min(c0 + j, c1 - 1);
@@ -1046,8 +1053,14 @@ __global__ __launch_bounds__(256, BF16IO ? 3 : 2) void kda_scan_output_kernel(Pa
     for (int kb = 0; kb < 4; ++kb)
       in[j].q[kb] = load_frag<BF16IO>(p.scan_q, qbase + c * (4 * 64 * 8) + kb * 64 * 8);
     if (m < end - (start + c * kC)) {
-      in[j].oz[0] = load4<BF16IO>(p.o, obase + c * kC * vstride);
-      in[j].oz[1] = load4<BF16IO>(p.o, obase + c * kC * vstride + 16);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t idx = obase + c * kC * vstride + 16 * i;
+        if constexpr (BF16IO)
+          in[j].oz[i] = *reinterpret_cast<const u32x2*>(static_cast<const unsigned short*>(p.o) + idx);
+        else
+          in[j].oz[i] = load4<false>(p.o, idx);
+      }
     }
   }
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -1060,8 +1073,17 @@ __global__ __launch_bounds__(256, BF16IO ? 3 : 2) void kda_scan_output_kernel(Pa
       acc = mfma32(sa[i][1], in[j].q[1], acc);
       acc = mfma32(sa[i][2], in[j].q[2], acc);
       acc = mfma32(sa[i][3], in[j].q[3], acc);
-      if (c < c1 && m < end - (start + c * kC))
-        store4<BF16IO>(p.o, obase + c * kC * vstride + 16 * i, acc + in[j].oz[i]);
+      if (c < c1 && m < end - (start + c * kC)) {
+        f32x4 oz;
+        if constexpr (BF16IO) {
+          const u32x2 w = in[j].oz[i];
+          oz = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                     __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+        } else {
+          oz = in[j].oz[i];
+        }
+        store4<BF16IO>(p.o, obase + c * kC * vstride + 16 * i, acc + oz);
+      }
     }
   }
 }
