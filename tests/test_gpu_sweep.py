@@ -16,7 +16,7 @@ from kda_testlib import rel_err, run_gpu, run_oracle
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
-CASES = 24
+CASES = 32
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -52,9 +52,12 @@ def draw(seed):
     geo = rng.random()
     if geo < 0.35:
         kw["segment_chunks"] = int(rng.choice([1, 2, 3, 5, 8]))
+        rows = int(rng.choice([0, 64, 128]))
+        if rows:
+            kw["rows_per_workgroup"] = rows
     elif geo < 0.55:
         kw["segment_chunks"] = -1
-        kw["rows_per_workgroup"] = int(rng.choice([16, 32, 64]))
+        kw["rows_per_workgroup"] = int(rng.choice([16, 32, 64, 128]))
     if rng.random() < 0.2:
         kw["checkpoint_every"] = int(rng.choice([16, 32, 64]))
     return x, kw
