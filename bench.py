@@ -330,7 +330,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the KDA prefill path has no multi-GPU "
-              "component in this build (heads shard across GPUs with no communication).",
+              "component (heads would shard across GPUs with no communication).",
               file=sys.stderr)
         sys.exit(2)
 
