@@ -5,7 +5,7 @@ and "SM120a prefill subset", names three optional in-kernel transforms:
 ``use_qk_l2norm_in_kernel``, ``beta_is_logit`` and the in-kernel lower-bound gate
 (``use_gate_in_kernel`` with ``A_log[H]``, ``dt_bias[H,128]`` and ``lower_bound`` in
 [-5, 0)). The page gives their inputs but not their formulas; the readings below are
-the plainest ones consistent with the pages, each marked "Reading" below.
+the plainest ones consistent with the pages, each stated with its function below.
 """
 
 import numpy as np
