@@ -124,8 +124,11 @@ typedef struct kda_prefill_args {
   uint32_t flags;        /* KDA_FLAG_* */
 
   /* Launch geometry: value rows handled by one workgroup of the recurrence (each
-     compute wave owns 16 rows). 0 = automatic; 16/32/64/128 force it. For a given
-     segment_chunks, results are bitwise identical for every choice. */
+     compute wave owns 16 rows). 0 = automatic: in the serial form the smallest of 16,
+     32 and 64 that keeps N * H * 128 / rows within the device's compute units, else
+     128 for BF16 I/O (64 for FP32); in the segmented form 64, or 128 for BF16 I/O
+     past N * H = 32. 16/32/64/128 force it. For a given segment_chunks, results are
+     bitwise identical for every choice. */
   int32_t rows_per_workgroup;
 
   /* Time segments of the recurrence. The chunk-to-chunk carry is affine in the state,

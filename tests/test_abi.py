@@ -184,6 +184,11 @@ def test_plan_follows_the_slice_rule():
     p = kda.kda_prefill_plan(fake(H=96, T=8192), 256)
     assert p["rows_per_workgroup"] == 64 and p["recurrence_workgroups"] == 192
     assert p["prepare_workgroups"] == 512 * 96
+    # Past one round of 64-row slices, whole heads (BF16 I/O): 8 x 24 pairs.
+    v = kda.kda_prefill_plan(fake(H=24, T=20000, N=8, varlen=True), 256)
+    assert v["rows_per_workgroup"] == 128 and v["waves_per_workgroup"] == 12
+    f32 = kda.kda_prefill_plan(fake(H=24, T=20000, N=8, varlen=True, io=kda.KDA_FP32), 256)
+    assert f32["rows_per_workgroup"] == 64
     # serial grid: whole rounds of 8 (sequence, head) pairs, each with its row blocks
     assert kda.kda_prefill_plan(fake(H=6, rows_per_workgroup=64), 256)["recurrence_workgroups"] == 16
     assert status(fake(rows_per_workgroup=128)) == 0
