@@ -91,6 +91,14 @@ def test_out_of_range_slot_starts_from_zero_and_writes_nothing():
 
 
 @pytest.mark.parametrize("L", [-1, 2])
+def test_pool_whole_head_workgroups(L):
+    # 128 value rows per workgroup (eight compute waves), serial and segmented, with an
+    # out-of-range slot and checkpoints in the serial case.
+    pool_case([4, 0, 9], segment_chunks=L, rows_per_workgroup=128,
+              **({"checkpoint_every": 32} if L < 0 else {}))
+
+
+@pytest.mark.parametrize("L", [-1, 2])
 def test_seq_order_changes_nothing(L):
     import torch
 
