@@ -98,6 +98,17 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Record tiles are stored non-temporally: a record is read once, by the recurrence
+// launch, long after it is written. Measured against plain stores (bitwise the same
+// results): the recurrence at T = 8192 took 286 instead of 303 us at H=96, 133 instead
+// of 147 us at H=24, and a whole H=6 call 72 instead of 74 us (H=12 alone lost ~2 us),
+// because dirty record lines no longer wait in L2 to be written back while the
+// recurrence streams.
+template <typename V>
+__device__ __forceinline__ void store_record(unsigned char* at, V v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(at));
+}
+
 // DPP within 16-lane rows: lane r receives lane r - N of its row (0 past the row start),
 // or lane N of its row.
 template <int N>
@@ -320,6 +331,7 @@ __global__ __launch_bounds__(256, 8) void kda_prepare_kernel(Params p) {
       f32x2 v;
       v[0] = E15[e];
       v[1] = E15[e + 1];
+      // (8-byte pieces stay ordinary stores: non-temporal ones write partial lines)
       *reinterpret_cast<f32x2*>(rec + kOffD + L * 8) = v;
     }
   }
@@ -358,7 +370,7 @@ __global__ __launch_bounds__(256, 8) void kda_prepare_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         out[4 * half + j] = sKe[4 * (L >> 4) + j][16 * (2 * bp + half) + (L & 15)];
-    *reinterpret_cast<u32x4*>(rec + kOffKeT + 16 * tid) = *reinterpret_cast<const u32x4*>(out);
+    store_record(rec + kOffKeT + 16 * tid, *reinterpret_cast<const u32x4*>(out));
   }
   lds_barrier();
 
@@ -431,13 +443,13 @@ __global__ __launch_bounds__(256, 8) void kda_prepare_kernel(Params p) {
     }
     const u32x2 k0 = __builtin_bit_cast(u32x2, kn[0]), k1 = __builtin_bit_cast(u32x2, kn[1]);
     const u32x2 q0 = __builtin_bit_cast(u32x2, qt[0]), q1 = __builtin_bit_cast(u32x2, qt[1]);
-    *reinterpret_cast<u32x4*>(rec + kOffKn + kb * 1024 + lane * 16) = u32x4{k0[0], k0[1], k1[0], k1[1]};
-    *reinterpret_cast<u32x4*>(rec + kOffQt + kb * 1024 + lane * 16) = u32x4{q0[0], q0[1], q1[0], q1[1]};
+    store_record(rec + kOffKn + kb * 1024 + lane * 16, u32x4{k0[0], k0[1], k1[0], k1[1]});
+    store_record(rec + kOffQt + kb * 1024 + lane * 16, u32x4{q0[0], q0[1], q1[0], q1[1]});
     if (wave == 0) {  // [L 64][Mb j 4, A_qk j 4]
       const f32x4 arow = *reinterpret_cast<const f32x4*>(&sA[m][4 * grp]);
       const u32x2 mb = __builtin_bit_cast(u32x2, pack4(mrow));
       const u32x2 aq = __builtin_bit_cast(u32x2, pack4(arow));
-      *reinterpret_cast<u32x4*>(rec + kOffMbAq + 16 * lane) = u32x4{mb[0], mb[1], aq[0], aq[1]};
+      store_record(rec + kOffMbAq + 16 * lane, u32x4{mb[0], mb[1], aq[0], aq[1]});
     }
   }
 }
