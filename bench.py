@@ -242,32 +242,89 @@ def time_config(x, steps, warmup, device, hip, **extra):
                 serial=serial, per_call_us=per_call)
 
 
-def cpu_baseline(x, budget_s=10.0, max_reps=30):
-    """The FP64 oracle on the host, one thread, over the whole workload: repeated until
-    about budget_s seconds of CPU work (at least one run), median reported."""
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
+_ORACLE_X = None  # the workload the pool's workers read (inherited through fork)
+
+
+def _oracle_block(h):
+    """One (sequence, head) block of the FP64 oracle: head h of a fixed-layout workload
+    with B = 1, the oracle as it stands, on one thread. Returns seconds."""
     from oracle import kda_recurrence_fp64
 
-    times = []
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    x = _ORACLE_X
+    sl = lambda a: None if a is None else a[:, :, h:h + 1]
+    s0 = None if x.state0 is None else x.state0[:, h:h + 1]
+    t = time.perf_counter()
+    kda_recurrence_fp64(sl(x.q), sl(x.k), sl(x.v), sl(x.g), x.beta[:, :, h:h + 1],
+                        state0=s0, scale=x.scale)
+    return time.perf_counter() - t
+
+
+def _one_thread():
     try:
-        if ctx:
-            ctx.__enter__()
-        while not times or (sum(times) < budget_s and len(times) < max_reps):
+        from threadpoolctl import threadpool_limits
+
+        threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        pass
+
+
+def host_cores():
+    """Cores this process may run on, capped at 16 (the host share of one GPU)."""
+    avail = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    return avail, max(1, min(avail, cap, 16))
+
+
+def time_oracle(x, budget_s, max_reps, workers):
+    """Wall seconds of the whole workload through the oracle, one (sequence, head) block
+    per task on `workers` processes (one BLAS thread each), repeated until about
+    budget_s seconds of wall time (at least once). Returns (median wall s, reps, summed
+    per-block CPU seconds of one rep)."""
+    import multiprocessing as mp
+
+    global _ORACLE_X
+    _ORACLE_X = x
+    ctx = mp.get_context("fork")
+    walls, cpu = [], 0.0
+    with ctx.Pool(processes=workers, initializer=_one_thread) as pool:
+        while not walls or (sum(walls) < budget_s and len(walls) < max_reps):
             t = time.perf_counter()
-            kda_recurrence_fp64(x.q, x.k, x.v, x.g, x.beta, **x.oracle_kwargs())
-            times.append(time.perf_counter() - t)
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    med = statistics.median(times)
-    return dict(value=round(x.tokens() / med, 1), unit="tokens/s", cores=1, kind="oracle",
-                sample=f"whole {x.name} workload ({x.tokens()} tokens x {x.H} heads), "
-                       f"FP64 NumPy token recurrence, median of {len(times)} runs "
-                       f"({med:.2f} s each, {sum(times):.1f} s total), 1 thread")
+            per = pool.map(_oracle_block, range(x.H), chunksize=1)
+            walls.append(time.perf_counter() - t)
+            cpu = sum(per)
+    _ORACLE_X = None
+    return statistics.median(walls), len(walls), cpu
+
+
+def cpu_baseline(x, x_full=None, budget_s=10.0, max_reps=30):
+    """The FP64 oracle timed on the host's cores: a process pool over the workload's
+    (sequence, head) blocks (heads are independent), one thread per process. The bench
+    workload is repeated for about budget_s seconds; x_full (the 96-head workload) is
+    timed once in full. A one-process run of the same blocks gives the single-core
+    figure."""
+    avail, cores = host_cores()
+    workers = min(cores, x.H)
+    wall, reps, cpu_s = time_oracle(x, budget_s, max_reps, workers)
+    th = x.tokens() * x.H
+    out = dict(value=round(x.tokens() / wall, 1), unit="tokens/s", cores=workers,
+               kind="oracle",
+               sample=f"whole {x.name} workload ({x.tokens()} tokens x {x.H} heads), FP64 "
+                      f"NumPy token recurrence, one (sequence, head) block per task on "
+                      f"{workers} processes (one thread each; {avail} host cores visible, "
+                      f"{cores} used at most), median wall time of {reps} runs "
+                      f"({wall:.3f} s each)",
+               wall_s=round(wall, 4), s_per_token_head=cpu_s / th,
+               one_core_tokens_per_s=round(x.tokens() / cpu_s, 1),
+               host_cores_visible=avail)
+    if x_full is not None:
+        workers_f = min(cores, x_full.H)
+        wall_f, _, cpu_f = time_oracle(x_full, 0.0, 1, workers_f)
+        th_f = x_full.tokens() * x_full.H
+        out["full_96_heads"] = dict(
+            workload=f"{x_full.name}: T={x_full.T} H={x_full.H}, every head",
+            wall_s=round(wall_f, 3), tokens_per_s=round(x_full.tokens() / wall_f, 1),
+            cores=workers_f, cpu_s=round(cpu_f, 2), s_per_token_head=cpu_f / th_f)
+    return out
 
 
 def progress(msg):
@@ -452,12 +509,22 @@ def main():
             if "alg_flop" in v:
                 v["mfma_frac_of_measured_gemm"] = round(v["alg_flop"] / t / (gemm_tflops * 1e12), 5)
     if "config1" in per_config and "config3" in per_config:
-        per_config["head_scaling_t96_over_t6"] = round(
-            per_config["config3"]["us"] / per_config["config1"]["us"], 3)
+        c1, c3 = per_config["config1"], per_config["config3"]
+        # t(H=96) / t(H=6) by step time, by warm per-call medians and by per-call medians
+        # with L2 and the 256 MB MALL flushed before each call (H=6's 63 MB of inputs
+        # fit in the MALL when warm).
+        per_config["head_scaling_t96_over_t6"] = round(c3["us"] / c1["us"], 3)
+        per_config["head_scaling_warm_per_call"] = round(
+            c3["per_call_us"]["warm"]["median"] / c1["per_call_us"]["warm"]["median"], 3)
+        per_config["head_scaling_flushed_per_call"] = round(
+            c3["per_call_us"]["flushed"]["median"] / c1["per_call_us"]["flushed"]["median"], 3)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(x)
-    if cpu:
-        progress(f"cpu_baseline: {cpu['value']} tokens/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        x3 = kda_synth.config(3) if args.config != 3 else None
+        cpu = cpu_baseline(x, x3)
+        del x3
+        progress(f"cpu_baseline: {cpu}")
 
     line = {
         "metric": "KDA prefill tokens/s at T=8192 (H=6 default; H=12/96 under per_config)",

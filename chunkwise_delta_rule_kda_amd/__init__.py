@@ -269,6 +269,106 @@ def kda_debug_check_cu_seqlens(cu_seqlens, T, stream=None):
         cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(T), s)
 
 
+def _validate(q, k, v, g, beta, state_in, cu_seqlens, A_log, dt_bias, lower_bound,
+              state_dtype, o, state_out, workspace, checkpoint_every, state_checkpoints,
+              checkpoint_cu_starts, ssm_state_indices, seq_order):
+    """Every check the C layer cannot make (it sees pointers, not sizes or devices),
+    before any pointer is passed on. Shapes, dtypes and layouts are checked first and
+    devices last. Returns (N, state dtype)."""
+    import torch
+
+    def need(cond, status, msg):
+        if not cond:
+            raise KdaError(status, msg)
+
+    need(isinstance(q, torch.Tensor) and q.dim() == 4, 2, "q must be a [B, T, H, 128] tensor")
+    B, T, H, D = q.shape
+    need(D == HEAD_DIM, 2, f"head dimension {D}, only {HEAD_DIM} is supported")
+    _dtype_code(q.dtype)
+    for name, t, shape in (("k", k, q.shape), ("v", v, q.shape), ("g", g, q.shape),
+                           ("beta", beta, (B, T, H))):
+        need(isinstance(t, torch.Tensor), 2, f"{name} must be a tensor")
+        need(tuple(t.shape) == tuple(shape), 2, f"{name} has shape {tuple(t.shape)}, "
+             f"expected {tuple(shape)}")
+        need(t.dtype == q.dtype, 3, f"{name} is {t.dtype}, q is {q.dtype}")
+    if cu_seqlens is not None:
+        need(cu_seqlens.dtype == torch.int64, 3, "cu_seqlens must be int64")
+        need(cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2, 2,
+             "cu_seqlens must be a 1-D tensor of N + 1 >= 2 offsets")
+        need(B == 1, 2, f"packed varlen needs B = 1 (got {B})")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if (A_log is None) != (dt_bias is None):
+        raise KdaError(4, "the in-kernel gate needs both A_log and dt_bias")
+    if A_log is not None:
+        need(lower_bound is not None, 4, "the in-kernel gate needs lower_bound")
+        need(A_log.dtype == torch.float32 and dt_bias.dtype == torch.float32, 3,
+             "A_log and dt_bias must be float32")
+        need(tuple(A_log.shape) == (H,), 2, f"A_log has shape {tuple(A_log.shape)}, "
+             f"expected ({H},)")
+        need(tuple(dt_bias.shape) == (H, D), 2, f"dt_bias has shape "
+             f"{tuple(dt_bias.shape)}, expected ({H}, {D})")
+    if state_dtype is None:
+        state_dtype = state_in.dtype if state_in is not None else q.dtype
+    _dtype_code(state_dtype)
+    if state_in is not None:
+        need(state_in.dtype == state_dtype, 3, f"state_in is {state_in.dtype}, the state "
+             f"dtype is {state_dtype}")
+        if ssm_state_indices is None:
+            need(tuple(state_in.shape) == (N, H, D, D), 2, f"state_in has shape "
+                 f"{tuple(state_in.shape)}, expected ({N}, {H}, {D}, {D})")
+        else:
+            need(state_in.dim() == 4 and tuple(state_in.shape[1:]) == (H, D, D), 2,
+                 "a state pool needs state_in [N_pool, H, 128, 128]")
+            need(state_in.shape[0] >= 1 and state_in[0].is_contiguous(), 2,
+                 "each state pool slot must be contiguous")
+            need(state_in.stride(0) % 8 == 0, 2, "the state pool's slot pitch must be a "
+                 "multiple of 8 elements")
+    elif ssm_state_indices is not None:
+        raise KdaError(10, "a state pool needs state_in")
+    if o is not None:
+        need(tuple(o.shape) == tuple(q.shape) and o.dtype == q.dtype, 2,
+             f"o must be {tuple(q.shape)} of {q.dtype}")
+    if state_out is not None:
+        if ssm_state_indices is not None:
+            need(state_out is state_in or state_out.data_ptr() == state_in.data_ptr(), 6,
+                 "with a state pool, state_out must be None or state_in")
+        need(tuple(state_out.shape) == (N, H, D, D) or state_out is state_in, 2,
+             f"state_out must be ({N}, {H}, {D}, {D})")
+        need(state_out.dtype == state_dtype, 3, f"state_out is {state_out.dtype}, the "
+             f"state dtype is {state_dtype}")
+    if state_checkpoints is not None:
+        need(state_checkpoints.dim() == 4 and tuple(state_checkpoints.shape[1:]) == (H, D, D),
+             2, "state_checkpoints must be [rows, H, 128, 128]")
+        need(state_checkpoints.dtype == state_dtype, 3, "state_checkpoints must have the "
+             "state dtype")
+    if checkpoint_cu_starts is not None:
+        need(checkpoint_cu_starts.dtype == torch.int64 and
+             tuple(checkpoint_cu_starts.shape) == (N + 1,), 2,
+             f"checkpoint_cu_starts must be int64 [{N + 1}]")
+    if checkpoint_every and checkpoint_every % 16:
+        raise KdaError(10, f"checkpoint_every {checkpoint_every} is not a multiple of 16")
+    for name, t in (("ssm_state_indices", ssm_state_indices), ("seq_order", seq_order)):
+        if t is not None:
+            need(t.dtype == torch.int32 and tuple(t.shape) == (N,), 3,
+                 f"{name} must be an int32 tensor of N={N} entries")
+    tensors = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+               ("state_in", state_in), ("cu_seqlens", cu_seqlens), ("A_log", A_log),
+               ("dt_bias", dt_bias), ("o", o), ("state_out", state_out),
+               ("workspace", workspace), ("state_checkpoints", state_checkpoints),
+               ("checkpoint_cu_starts", checkpoint_cu_starts),
+               ("ssm_state_indices", ssm_state_indices), ("seq_order", seq_order)]
+    for name, t in tensors:
+        if t is None or (name == "state_in" and ssm_state_indices is not None):
+            continue
+        need(t.is_contiguous(), 2, f"{name} must be contiguous")
+    for name, t in tensors:
+        if t is None:
+            continue
+        need(t.is_cuda and t.device == q.device, 2,
+             f"{name} must be a CUDA tensor on {q.device} (got {t.device})")
+    return N, state_dtype
+
+
 def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                 A_log=None, dt_bias=None, lower_bound=None, l2norm_qk=False,
                 beta_is_logit=False, output_final_state=True, state_dtype=None, o=None,
@@ -297,18 +397,15 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
     """
     import torch
 
+    N, st_dtype = _validate(q, k, v, g, beta, state_in, cu_seqlens, A_log, dt_bias,
+                            lower_bound, state_dtype, o, state_out, workspace,
+                            checkpoint_every, state_checkpoints, checkpoint_cu_starts,
+                            ssm_state_indices, seq_order)
     lib = load_library()
     B, T, H, D = q.shape
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    state_dtype = st_dtype
     io = _dtype_code(q.dtype)
-    if state_dtype is None:
-        state_dtype = state_in.dtype if state_in is not None else q.dtype
     st = _dtype_code(state_dtype)
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
-        if t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise KdaError(3, f"{name} must be a contiguous CUDA tensor of {q.dtype}")
-    if cu_seqlens is not None and cu_seqlens.dtype != torch.int64:
-        raise KdaError(3, "cu_seqlens must be int64")
     flags = 0
     if l2norm_qk:
         flags |= KDA_FLAG_L2NORM_QK
@@ -316,19 +413,10 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
         flags |= KDA_FLAG_BETA_IS_LOGIT
     if A_log is not None:
         flags |= KDA_FLAG_GATE_IN_KERNEL
-        if lower_bound is None:
-            raise KdaError(4, "the in-kernel gate needs lower_bound")
     if o is None:
         o = torch.empty_like(v)
     pool_slots = pool_pitch = 0
-    for name, t in (("ssm_state_indices", ssm_state_indices), ("seq_order", seq_order)):
-        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or t.numel() != N):
-            raise KdaError(3, f"{name} must be an int32 CUDA tensor of N={N} entries")
     if ssm_state_indices is not None:
-        if state_in is None or state_in.dim() != 4 or state_in.shape[1:] != (H, D, D):
-            raise KdaError(2, "a state pool needs state_in [N_pool, H, 128, 128]")
-        if not state_in[0].is_contiguous():
-            raise KdaError(2, "each state pool slot must be contiguous")
         pool_slots, pool_pitch = state_in.shape[0], state_in.stride(0)
         state_out = state_in
     if state_out is None and output_final_state:

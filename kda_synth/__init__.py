@@ -23,7 +23,11 @@ values are exactly representable in that dtype, so both sides receive identical 
 Stress families (the K3 decay page, section "Numerical experiments on H200", generalised
 to per-channel decay): ``weak_decay`` (g = -0.05 * logistic(N(0,1)), initial state
 N(0,1)), ``correlated`` (one shared unit key, g = -0.01, beta = 0.5), ``floor``
-(g = -5 everywhere) and ``gate_weak`` (config 4's raw-gate recipe with lower_bound -0.1).
+(g = -5 everywhere), ``gate_weak`` (config 4's raw-gate recipe with lower_bound -0.1) and
+``weak_carry`` (g = -gscale * logistic(N(0,1)), beta = bscale * logistic(N(0,1)),
+initial state 0.1 * N(0,1); small enough decay and write strength that the transition
+over hundreds of tokens stays of order 0.1-0.5, so that a time segment's start state
+visibly shapes every later output of the segment).
 """
 
 from dataclasses import dataclass, field, replace
@@ -183,9 +187,24 @@ def config(i, *, T=None, H=None, B=None, lengths=None, seed=None, dtype=None):
                           state_sd)
 
 
-def stress(family, *, T, H, B=1, seed=100, dtype="bf16", lengths=None):
-    """Stress inputs that make the inter-chunk carry and the inverse matter."""
+def stress(family, *, T, H, B=1, seed=100, dtype="bf16", lengths=None, gscale=2e-3,
+           bscale=0.2):
+    """Stress inputs that make the inter-chunk carry and the inverse matter. gscale and
+    bscale are the decay and write-strength scales of ``weak_carry``."""
     rng = np.random.default_rng(seed)
+    if family == "weak_carry":
+        shp = (B, T, H, D)
+        q = _unit_rows(rng.standard_normal(shp))
+        k = _unit_rows(rng.standard_normal(shp))
+        v = rng.standard_normal(shp)
+        g = -gscale * _logistic(rng.standard_normal(shp))
+        beta = bscale * _logistic(rng.standard_normal((B, T, H)))
+        state0 = 0.1 * rng.standard_normal((B, H, D, D))
+        return KdaInputs(
+            name="weak_carry", q=_store(q, dtype), k=_store(k, dtype), v=_store(v, dtype),
+            g=_store(g, dtype), beta=_store(beta, dtype), state0=_store(state0, dtype),
+            dtype=dtype, state_dtype=dtype, meta=dict(gscale=gscale, bscale=bscale),
+        )
     if family == "weak_decay":
         return _normal_family("weak_decay", rng, B, T, H, dtype, 1.0, decay=-0.05)
     if family == "floor":
