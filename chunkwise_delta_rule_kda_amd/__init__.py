@@ -6,6 +6,8 @@ library has not been built this module raises on the first call (there is no fal
 
 Entry points (same names as the C ABI):
     kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, ...) -> (o, state_out)
+    kda_prefill_no_alloc(...): the same with the library's static device scratch as the
+        workspace (no workspace argument; the outputs are still the caller's or torch's)
     kda_prefill_workspace_bytes(...), kda_prefill_check(...), kda_prefill_plan(...)
     kda_status_string(status), kda_last_error(), kda_debug_check_cu_seqlens(cu, T)
 """
@@ -19,6 +21,7 @@ __all__ = [
     "lib_path",
     "load_library",
     "kda_prefill",
+    "kda_prefill_no_alloc",
     "kda_prefill_args",
     "kda_prefill_workspace_bytes",
     "kda_prefill_check",
@@ -126,6 +129,8 @@ class kda_plan_info(ctypes.Structure):
     ]
 
 
+KDA_NO_ALLOC_SCRATCH_BYTES = 64 << 20  # include/kda.h
+
 ABI_VERSION = 6  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
 
 
@@ -150,6 +155,8 @@ def load_library():
     P = ctypes.POINTER(kda_prefill_args)
     lib.kda_prefill.argtypes = [P, ctypes.c_void_p]
     lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill_no_alloc.argtypes = [P, ctypes.c_void_p]
+    lib.kda_prefill_no_alloc.restype = ctypes.c_int
     lib.kda_prefill_check.argtypes = [P]
     lib.kda_prefill_check.restype = ctypes.c_int
     lib.kda_prefill_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
@@ -374,7 +381,8 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                 beta_is_logit=False, output_final_state=True, state_dtype=None, o=None,
                 state_out=None, workspace=None, rows_per_workgroup=0, segment_chunks=0,
                 checkpoint_every=0, state_checkpoints=None, checkpoint_cu_starts=None,
-                ssm_state_indices=None, seq_order=None, stream=None, trace_events=None):
+                ssm_state_indices=None, seq_order=None, stream=None, trace_events=None,
+                _no_alloc=False):
     """Chunkwise KDA prefill forward on the current (or given) HIP stream.
 
     q, k, v, g: [B, T, H, 128] bf16 or fp32 CUDA tensors (contiguous); beta [B, T, H].
@@ -450,14 +458,30 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                      ssm_state_indices=ssm_state_indices, state_pool_slots=pool_slots,
                      state_slot_pitch=pool_pitch, seq_order=seq_order,
                      trace_events=trace_events)
-    need = kda_prefill_workspace_bytes(args)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    args.workspace = workspace.data_ptr()
-    args.workspace_bytes = workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    _raise_if(lib.kda_prefill(ctypes.byref(args), stream))
+    if _no_alloc:
+        if workspace is not None:
+            raise KdaError(7, "kda_prefill_no_alloc takes no workspace")
+        _raise_if(lib.kda_prefill_no_alloc(ctypes.byref(args), stream))
+    else:
+        need = kda_prefill_workspace_bytes(args)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel() * workspace.element_size()
+        _raise_if(lib.kda_prefill(ctypes.byref(args), stream))
     if checkpoint_every:
         return o, state_out, state_checkpoints
     return o, state_out
+
+
+def kda_prefill_no_alloc(q, k, v, g, beta, state_in=None, cu_seqlens=None, **kw):
+    """kda_prefill through the C entry point of the same name: the workspace is the
+    library's static device scratch (KDA_NO_ALLOC_SCRATCH_BYTES per device), so the
+    library allocates nothing. Outputs not passed in (o, state_out) are still allocated
+    here with torch; pass them for a call that allocates nothing at all. Calls needing
+    more workspace than the scratch holds raise KdaError(KDA_ERR_WORKSPACE)."""
+    if kw.get("workspace") is not None:
+        raise KdaError(7, "kda_prefill_no_alloc takes no workspace")
+    return kda_prefill(q, k, v, g, beta, state_in, cu_seqlens, _no_alloc=True, **kw)

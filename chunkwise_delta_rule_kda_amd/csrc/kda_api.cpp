@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
@@ -14,6 +15,11 @@
 
 #include "kda.h"
 #include "kda_internal.h"
+
+// Workspace of kda_prefill_no_alloc: one copy per device, alive until the process ends.
+// In host code this name is only a handle for hipGetSymbolAddress; the device address
+// it resolves to (per device) is what kernels and copies use.
+static __device__ __align__(256) unsigned char scratch[KDA_NO_ALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -283,6 +289,28 @@ int cu_count_current(void) {
   return n;
 }
 
+// Device address of `scratch` on the current device, resolved once per device (with
+// that device current) and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+kda_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(KDA_ERR_HIP, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -535,6 +563,30 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s", hipGetErrorString(e));
   return KDA_OK;
+}
+
+kda_status kda_prefill_no_alloc(const kda_prefill_args* a, void* stream) {
+  g_last_error.clear();
+  kda_status s = check_shape(a);
+  if (s != KDA_OK) return s;
+  if (a->workspace)
+    return fail(KDA_ERR_WORKSPACE, "kda_prefill_no_alloc uses the library's static scratch: "
+                                   "pass workspace = NULL");
+  const size_t need = workspace_need(a);
+  if (need > KDA_NO_ALLOC_SCRATCH_BYTES)
+    return fail(KDA_ERR_WORKSPACE,
+                "the call needs %zu bytes of workspace, the static scratch holds %llu "
+                "(use kda_prefill with a caller-allocated workspace)",
+                need, (unsigned long long)KDA_NO_ALLOC_SCRATCH_BYTES);
+  kda_prefill_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (need > 0) {
+    s = scratch_on_current_device(&b.workspace);
+    if (s != KDA_OK) return s;
+    b.workspace_bytes = KDA_NO_ALLOC_SCRATCH_BYTES;
+  }
+  return kda_prefill(&b, stream);
 }
 
 kda_status kda_debug_check_cu_seqlens(const int64_t* cu, int64_t N, int64_t T, void* stream) {

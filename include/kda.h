@@ -29,8 +29,9 @@
  *
  * Ownership: the caller allocates every buffer (inputs, outputs, workspace). The library
  * allocates nothing, keeps no per-call caches and holds no global state besides a
- * per-device compute-unit count. All pointers in kda_prefill_args are device pointers
- * unless stated otherwise.
+ * per-device compute-unit count and, for kda_prefill_no_alloc, one static device array
+ * per device (its scratch, see there). All pointers in kda_prefill_args are device
+ * pointers unless stated otherwise.
  *
  * Errors: every entry point returns a kda_status; nothing aborts or throws across the
  * ABI. Host-checkable violations are rejected before any launch. Device-side contract
@@ -272,6 +273,19 @@ kda_status kda_prefill_check(const kda_prefill_args *a);
    Asynchronous: no device synchronisation, no device-to-host read of cu_seqlens.
    Launch geometry uses the upper bound (T + 15 N) / 16 on the total chunk count. */
 kda_status kda_prefill(const kda_prefill_args *a, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+   serving loops, harnesses that forbid hipMalloc): kda_prefill with the workspace taken
+   from a static device array of KDA_NO_ALLOC_SCRATCH_BYTES bytes that the library holds
+   on each device it runs on until the process ends (its address is resolved on the
+   first call on a device). a->workspace must be NULL; every other argument, and all
+   behaviour, is that of kda_prefill. Calls whose kda_prefill_workspace_bytes exceed
+   KDA_NO_ALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE before any launch. The call makes
+   no hipMalloc or hipFree. All calls on one device share its array and nothing in it
+   needs clearing between calls; calls that overlap in time on one device (on different
+   streams, or from several threads) race on it and must be serialised by the caller. */
+#define KDA_NO_ALLOC_SCRATCH_BYTES (64ull << 20)
+kda_status kda_prefill_no_alloc(const kda_prefill_args *a, void *stream);
 
 /* Static description of a status code. */
 const char *kda_status_string(kda_status s);
