@@ -40,8 +40,8 @@ FLOP_PREP_PER_TOKEN_HEAD = 2 * 2 * C * D
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 
-KERNEL_SOURCES = ["kda_prepare.hip", "kda_recurrence.hip", "kda_decode.hip", "kda_device.h",
-                  "kda_internal.h"]
+KERNEL_SOURCES = ["kda_prepare.hip", "kda_recurrence.hip", "kda_fused.hip", "kda_decode.hip",
+                  "kda_device.h", "kda_internal.h", "kda_recurrence_core.h", "kda_producer.h"]
 
 
 def kernel_hash():
@@ -108,10 +108,15 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+FUSE_PREPARE = 0  # --fuse-prepare
+
+
 def make_call(x, device, **extra):
     """Device inputs, outputs and workspace for one configuration (allocated once).
     extra: further kda_prefill keyword arguments (launch geometry)."""
     import torch
+
+    extra.setdefault("fuse_prepare", FUSE_PREPARE)
 
     import chunkwise_delta_rule_kda_amd as kda
     from tests.kda_testlib import to_device
@@ -380,6 +385,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step line")
     ap.add_argument("--no-head-sweep", action="store_true", help="skip the H=24/48 lines")
+    ap.add_argument("--fuse-prepare", type=int, default=0,
+                    help="0 automatic, 1 chunk preparation fused into the recurrence, -1 a "
+                         "separate preparation kernel")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter "
                          "calibration for rocprofv3 --pmc runs)")
@@ -396,6 +404,8 @@ def main():
     import chunkwise_delta_rule_kda_amd as kda
     import kda_synth
 
+    global FUSE_PREPARE
+    FUSE_PREPARE = args.fuse_prepare
     kda.load_library()
     device = torch.device("cuda:0")
     hip = HipEvents()

@@ -35,6 +35,7 @@ __all__ = [
     "KDA_FLAG_L2NORM_QK",
     "KDA_FLAG_GATE_IN_KERNEL",
     "KDA_FLAG_BETA_IS_LOGIT",
+    "KDA_FLAG_KEEP_RECORDS",
     "KDA_WS_RECORD",
     "STATUS",
 ]
@@ -44,6 +45,7 @@ KDA_FP32 = 1
 KDA_FLAG_L2NORM_QK = 1 << 0
 KDA_FLAG_GATE_IN_KERNEL = 1 << 1
 KDA_FLAG_BETA_IS_LOGIT = 1 << 2
+KDA_FLAG_KEEP_RECORDS = 1 << 3
 KDA_WS_RECORD = 13824
 HEAD_DIM = 128
 
@@ -106,6 +108,7 @@ class kda_prefill_args(ctypes.Structure):
         ("seq_order", ctypes.c_void_p),
         ("trace_events", ctypes.c_void_p),
         ("n_trace_events", ctypes.c_int32),
+        ("fuse_prepare", ctypes.c_int32),
     ]
 
 
@@ -126,12 +129,16 @@ class kda_plan_info(ctypes.Structure):
         ("decode", ctypes.c_int32),
         ("scan_affine_output", ctypes.c_int32),
         ("scan_output_offset", ctypes.c_size_t),
+        ("fused", ctypes.c_int32),
+        ("has_records", ctypes.c_int32),
+        ("records_offset", ctypes.c_size_t),
+        ("status_offset", ctypes.c_size_t),
     ]
 
 
 KDA_NO_ALLOC_SCRATCH_BYTES = 64 << 20  # include/kda.h
 
-ABI_VERSION = 6  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
+ABI_VERSION = 7  # the kda_prefill_args layout above (include/kda.h, KDA_ABI_VERSION)
 
 
 def lib_path():
@@ -217,7 +224,7 @@ def make_args(*, q=None, k=None, v=None, g=None, beta=None, state_in=None, cu_se
               rows_per_workgroup=0, segment_chunks=0, checkpoint_every=0,
               checkpoint_rows=0, state_checkpoints=None, checkpoint_cu_starts=None,
               ssm_state_indices=None, state_pool_slots=0, state_slot_pitch=0, seq_order=None,
-              trace_events=None):
+              trace_events=None, fuse_prepare=0):
     """Fill a kda_prefill_args from raw pointers (ints), tensors or None."""
     a = kda_prefill_args()
     a.q, a.k, a.v, a.g, a.beta = (_ptr(x) for x in (q, k, v, g, beta))
@@ -242,6 +249,7 @@ def make_args(*, q=None, k=None, v=None, g=None, beta=None, state_in=None, cu_se
     a.state_pool_slots = int(state_pool_slots)
     a.state_slot_pitch = int(state_slot_pitch)
     a.seq_order = _ptr(seq_order)
+    a.fuse_prepare = int(fuse_prepare)
     if trace_events is not None:
         arr = (ctypes.c_void_p * len(trace_events))(*trace_events)
         a._trace_keepalive = arr
@@ -382,7 +390,7 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                 state_out=None, workspace=None, rows_per_workgroup=0, segment_chunks=0,
                 checkpoint_every=0, state_checkpoints=None, checkpoint_cu_starts=None,
                 ssm_state_indices=None, seq_order=None, stream=None, trace_events=None,
-                _no_alloc=False):
+                fuse_prepare=0, keep_records=False, _no_alloc=False):
     """Chunkwise KDA prefill forward on the current (or given) HIP stream.
 
     q, k, v, g: [B, T, H, 128] bf16 or fp32 CUDA tensors (contiguous); beta [B, T, H].
@@ -421,6 +429,8 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
         flags |= KDA_FLAG_BETA_IS_LOGIT
     if A_log is not None:
         flags |= KDA_FLAG_GATE_IN_KERNEL
+    if keep_records:
+        flags |= KDA_FLAG_KEEP_RECORDS
     if o is None:
         o = torch.empty_like(v)
     pool_slots = pool_pitch = 0
@@ -457,7 +467,7 @@ def kda_prefill(q, k, v, g, beta, state_in=None, cu_seqlens=None, *, scale=None,
                      checkpoint_cu_starts=checkpoint_cu_starts,
                      ssm_state_indices=ssm_state_indices, state_pool_slots=pool_slots,
                      state_slot_pitch=pool_pitch, seq_order=seq_order,
-                     trace_events=trace_events)
+                     trace_events=trace_events, fuse_prepare=fuse_prepare)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     if _no_alloc:

@@ -7,21 +7,23 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libkda.so")
 
-SOURCES = ["kda_api.cpp", "kda_prepare.hip", "kda_recurrence.hip", "kda_decode.hip"]
-HEADERS = ["kda_internal.h", "kda_device.h"]
+SOURCES = ["kda_api.cpp", "kda_prepare.hip", "kda_recurrence.hip", "kda_fused.hip",
+           "kda_decode.hip"]
+HEADERS = ["kda_internal.h", "kda_device.h", "kda_recurrence_core.h", "kda_producer.h"]
 
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # packed-FP32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -36,23 +38,35 @@ def hipcc():
     return path
 
 
-def build(verbose=False, out=LIB, extra_flags=()):
-    """Compile every source into one shared library (always recompiles)."""
-    srcs = [os.path.join(HERE, s) for s in SOURCES]
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", HERE,
-           "-x", "hip", *srcs, "-o", tmp]
+def _run(cmd, what, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libkda.so")
+        raise RuntimeError(f"hipcc failed on {what}")
     if verbose and res.stderr.strip():
         # hipcc's host pass does not know the packed-fp32 feature; drop that noise
         lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
         if lines:
             sys.stderr.write("\n".join(lines) + "\n")
+
+
+def build(verbose=False, out=LIB, extra_flags=(), jobs=None):
+    """Compile every source (always recompiles, one hipcc per translation unit, in
+    parallel) and link them into one shared library."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", HERE]
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
+    with tempfile.TemporaryDirectory(prefix="kda_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [([hipcc(), *FLAGS, *extra_flags, *inc, "-x", "hip", "-c",
+                  os.path.join(HERE, s), "-o", o], s) for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            for f in [pool.submit(_run, c, s, verbose) for c, s in cmds]:
+                f.result()
+        tmp = out + ".tmp"
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+             "the link", verbose)
     os.replace(tmp, out)
     return out
 

@@ -81,7 +81,8 @@ kda_status check_shape(const kda_prefill_args* a) {
     return fail(KDA_ERR_DTYPE, "io_dtype %d", a->io_dtype);
   if (a->state_dtype != KDA_BF16 && a->state_dtype != KDA_FP32)
     return fail(KDA_ERR_DTYPE, "state_dtype %d", a->state_dtype);
-  const uint32_t known = KDA_FLAG_L2NORM_QK | KDA_FLAG_GATE_IN_KERNEL | KDA_FLAG_BETA_IS_LOGIT;
+  const uint32_t known = KDA_FLAG_L2NORM_QK | KDA_FLAG_GATE_IN_KERNEL | KDA_FLAG_BETA_IS_LOGIT |
+                         KDA_FLAG_KEEP_RECORDS;
   if (a->flags & ~known) return fail(KDA_ERR_FLAGS, "unknown flag bits 0x%x", a->flags & ~known);
   if (a->flags & KDA_FLAG_GATE_IN_KERNEL) {
     if (!a->A_log || !a->dt_bias)
@@ -151,8 +152,19 @@ struct Plan {
   size_t scan_phi = 0;       // offset of the BF16 transitions
   bool affine = false;       // affine-output segmented form (no checkpoints)
   size_t scan_q = 0;         // offset of Qt Phi^T per chunk (affine-output form)
+  bool fused = false;        // the recurrence prepares its own chunks (no prepare kernel)
+  bool has_records = false;  // the workspace holds the records
+  size_t status = 0;         // offset of the 256-byte status block
   size_t total = 0;
 };
+
+// The fused form (producer waves in the recurrence workgroups prepare the chunks) when
+// the caller asks for it. The automatic choice is the separate preparation kernel: on
+// MI355X the fused form's producers (one wave per chunk, about 12k cycles of dependent
+// work each) leave the compute waves waiting, 1.5-2x slower at every head count measured
+// (T = 8192, H = 6: 126 vs 72 us per call; H = 96: 811 vs 634 us), although it moves
+// only the algorithmic bytes.
+bool fused_form(const kda_prefill_args* a) { return a->fuse_prepare > 0; }
 
 // A few tokens per sequence (fixed layout, 1 <= T <= kDecodeMaxT, no checkpoints,
 // automatic geometry): the token-loop kernel, no workspace. An explicit
@@ -219,9 +231,14 @@ Plan make_plan(const kda_prefill_args* a) {
   pl.header = a->cu_seqlens ? round_up(static_cast<size_t>(a->N + 1) * 16 +
                                            static_cast<size_t>(a->N) * 4, 256)
                             : 0;
+  pl.fused = fused_form(a);
   pl.records = pl.header;
-  size_t end = pl.records + static_cast<size_t>(pl.max_chunks) * static_cast<size_t>(a->H) *
-                                static_cast<size_t>(kda::kRecord);
+  size_t end = pl.records;
+  if (!pl.fused || (a->flags & KDA_FLAG_KEEP_RECORDS)) {
+    pl.has_records = true;
+    end += static_cast<size_t>(pl.max_chunks) * static_cast<size_t>(a->H) *
+           static_cast<size_t>(kda::kRecord);
+  }
   if (pl.seg_len > 0) {
     const size_t slots = static_cast<size_t>(a->H) * static_cast<size_t>(pl.seg_stride);
     pl.scan_s = round_up(end, 256);
@@ -234,7 +251,8 @@ Plan make_plan(const kda_prefill_args* a) {
                             elem_size(a->io_dtype);
     }
   }
-  pl.total = end;
+  pl.status = round_up(end, 256);
+  pl.total = pl.status + 256;
   return pl;
 }
 
@@ -441,7 +459,19 @@ kda_status kda_prefill_plan(const kda_prefill_args* a, int32_t num_cus, kda_plan
   }
   out->scan_state_offset = pl.scan_s;
   out->scan_transition_offset = pl.scan_phi;
+  out->fused = pl.fused ? 1 : 0;
+  out->status_offset = pl.status;
+  out->records_offset = pl.has_records ? pl.records : 0;
+  out->has_records = pl.has_records ? 1 : 0;
+  if (pl.fused) {
+    out->prepare_workgroups = 0;
+    out->waves_per_workgroup = rows / 16 + 4;
+  }
   if (decode_form(a)) {
+    out->fused = 0;
+    out->status_offset = 0;
+    out->records_offset = 0;
+    out->has_records = 0;
     out->decode = 1;
     out->prepare_workgroups = 0;
     out->recurrence_workgroups = a->N * a->H;
@@ -507,6 +537,11 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
     p.ckpt_every = a->checkpoint_every / KDA_CHUNK;
     p.ckpt_rows = a->checkpoint_rows;
   }
+  if (pl.fused) {
+    p.fused = 1;
+    p.keep_records = (a->flags & KDA_FLAG_KEEP_RECORDS) ? 1 : 0;
+  }
+  p.status = reinterpret_cast<int*>(ws + pl.status);
   if (pl.seg_len > 0) {
     p.scan_s = reinterpret_cast<float*>(ws + pl.scan_s);
     p.scan_phi = reinterpret_cast<unsigned short*>(ws + pl.scan_phi);
@@ -536,7 +571,7 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
   }
   if (ev) e = hipEventRecord(ev[0], stream);
   if (e == hipSuccess && a->cu_seqlens) e = kda::launch_plan(p, auto_order, stream);
-  if (e == hipSuccess && a->T > 0) e = kda::launch_prepare(p, io_bf16, stream);
+  if (e == hipSuccess && a->T > 0 && !pl.fused) e = kda::launch_prepare(p, io_bf16, stream);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
   if (pl.seg_len == 0) {
     // whole rounds of 8 (sequence, head) pairs over the XCDs, each with its row blocks

@@ -83,6 +83,10 @@ struct Params {
   int64_t pool_slots;
   int64_t slot_pitch;         // elements between slots
   const int32_t* seq_order;   // [N] or null
+  // Fused form: the recurrence workgroups prepare their own chunks (no records in HBM).
+  int32_t fused;
+  int32_t keep_records;       // fused: also write each record to `records` (inspection)
+  int* status;                // fused: bit 0 set when an internal bounded wait timed out
 };
 
 // auto_order: null, or [N] int32 (N <= kAutoOrderMax) for the sequences by decreasing
@@ -92,6 +96,10 @@ hipError_t launch_prepare(const Params& p, bool io_bf16, hipStream_t stream);
 int recurrence_loader_waves(int compute_waves);
 hipError_t launch_recurrence(const Params& p, int64_t workgroups, bool io_bf16,
                              bool state_bf16, hipStream_t stream);
+// The recurrence launch of the fused form (p.fused): same workgroups, producer waves
+// instead of loader waves (kda_fused.hip).
+hipError_t launch_fused_recurrence(const Params& p, int64_t workgroups, bool io_bf16,
+                                   bool state_bf16, hipStream_t stream);
 hipError_t launch_combine(const Params& p, bool state_bf16, hipStream_t stream);
 hipError_t launch_scan_output(const Params& p, int64_t workgroups, bool io_bf16,
                               hipStream_t stream);

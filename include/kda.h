@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 #define KDA_HEAD_DIM 128 /* d_k = d_v = 128 */
 #define KDA_CHUNK 16     /* tokens per chunk */
 
@@ -86,7 +86,11 @@ enum {
      dt_bias and lower_bound in [-5, 0) */
   KDA_FLAG_GATE_IN_KERNEL = 1u << 1,
   /* beta <- sigmoid(beta) */
-  KDA_FLAG_BETA_IS_LOGIT = 1u << 2
+  KDA_FLAG_BETA_IS_LOGIT = 1u << 2,
+  /* fused form: also write every prepared record to the workspace's record area (for
+     inspection; the workspace then includes that area). The separate preparation
+     kernel always writes them. */
+  KDA_FLAG_KEEP_RECORDS = 1u << 3
 };
 
 typedef struct kda_prefill_args {
@@ -201,6 +205,16 @@ typedef struct kda_prefill_args {
      recurrence in the serial form). */
   void *const *trace_events;
   int32_t n_trace_events;
+
+  /* Where the chunk preparation runs. Positive: fused into the recurrence; four
+     producer waves in every recurrence workgroup prepare the chunks of its run from q,
+     k, g, beta (and copy its V tile) straight into the LDS ring its compute waves read,
+     one chunk per producer wave, handed over through LDS counters with bounded waits
+     (the prepared records never go through HBM). 0 (automatic) or negative: a separate
+     preparation kernel (one workgroup per chunk and head) writes the records to the
+     workspace first and the recurrence streams them back. Results differ only by
+     rounding. */
+  int32_t fuse_prepare;
 } kda_prefill_args;
 
 /*
@@ -215,11 +229,13 @@ typedef struct kda_prefill_args {
  *                                 seq_order (and N <= 256), the sequences by decreasing
  *                                 chunk count (ties by index), the order in which their
  *                                 work starts.
- *   [KDA_WS_HEADER, ...)          one KDA_WS_RECORD-byte record per (chunk c, head h)
- *                                 at index h * max_chunks + c, where c counts chunks
- *                                 over all sequences in order and max_chunks is the
- *                                 plan's bound (kda_prefill_plan): N * ceil(T / 16)
- *                                 for the fixed layout, (T + 15 N) / 16 for varlen.
+ *   [KDA_WS_HEADER, ...)          only with the separate preparation kernel or
+ *                                 KDA_FLAG_KEEP_RECORDS: one KDA_WS_RECORD-byte record
+ *                                 per (chunk c, head h) at index h * max_chunks + c,
+ *                                 where c counts chunks over all sequences in order and
+ *                                 max_chunks is the plan's bound (kda_prefill_plan):
+ *                                 N * ceil(T / 16) for the fixed layout, (T + 15 N) / 16
+ *                                 for varlen.
  *   scan_state_offset             segmented form only: FP32 [H][S] slots of 128 x 128,
  *                                 the start state (or zero-start end state) per
  *                                 segment, S = segments_per_head_bound; inside a slot,
@@ -238,6 +254,11 @@ typedef struct kda_prefill_args {
  *                                 2048 elements of the io dtype, Qt Phi^T of each
  *                                 chunk of a later segment (Phi from the segment start
  *                                 to the chunk start), in the record's Qt layout.
+ *   status_offset                 the last 256 bytes: int32 status. Bit 0 is set when a
+ *                                 bounded wait of the fused form timed out (an internal
+ *                                 failure; that call's outputs are then invalid). The
+ *                                 library never clears it: a caller that checks it
+ *                                 clears it before the call.
  * KDA_WS_HEADER = round_up((N + 1) * 16 + 4 N, 256) for varlen, 0 for the fixed layout.
  *
  * A record holds, for the chunk's 16 tokens (pad tokens of a short last chunk behave as
@@ -322,6 +343,10 @@ typedef struct kda_plan_info {
   int32_t decode;                  /* 1: the token-loop kernel (1 <= T <= 8, see above) */
   int32_t scan_affine_output;      /* 1: the affine-output segmented form */
   size_t scan_output_offset;
+  int32_t fused;                   /* 1: the chunk preparation runs in the recurrence */
+  int32_t has_records;             /* 1: the workspace holds the records */
+  size_t records_offset;           /* where they start (the header's end) */
+  size_t status_offset;            /* the 256-byte status block */
 } kda_plan_info;
 kda_status kda_prefill_plan(const kda_prefill_args *a, int32_t num_cus, kda_plan_info *out);
 

@@ -47,7 +47,7 @@ def test_record_size_matches_header():
 
 def test_abi_version_and_status_strings():
     lib = kda.load_library()
-    assert lib.kda_abi_version() == 6
+    assert lib.kda_abi_version() == 7
     for code in range(11):
         assert kda.kda_status_string(code) and kda.kda_status_string(code) != "unknown status"
     assert kda.kda_status_string(99) == "unknown status"
@@ -124,17 +124,30 @@ def test_aliasing_rejected():
 
 
 def test_workspace_checks():
-    a = fake(T=100, H=3)
-    need = kda.kda_prefill_workspace_bytes(a)
-    assert need == 7 * 3 * kda.KDA_WS_RECORD  # ceil(100/16) = 7 chunks, 3 heads
-    assert status(fake(T=100, H=3, workspace_bytes=need)) == 0
-    assert status(fake(T=100, H=3, workspace_bytes=need - 1)) == 7
-    assert status(fake(T=100, H=3, workspace=None)) == 7
-    assert status(fake(T=100, H=3, workspace=0x7F0000000000 + 8 * 256 * MB + 128)) == 7
-    # varlen: (T + 15 N) / 16 chunk records plus the 256-byte-rounded header
-    # (cu_chunks and cu_segs, 2 (N + 1) int64)
-    v = fake(T=100, H=3, N=5, varlen=True)
-    assert kda.kda_prefill_workspace_bytes(v) == 256 + ((100 + 15 * 5) // 16) * 3 * kda.KDA_WS_RECORD
+    # Separate preparation kernel (the default): ceil(100/16) = 7 chunk records for each
+    # of 3 heads, then the 256-byte status block.
+    two = dict(fuse_prepare=0)
+    need = kda.kda_prefill_workspace_bytes(fake(T=100, H=3, **two))
+    assert need == 7 * 3 * kda.KDA_WS_RECORD + 256
+    assert status(fake(T=100, H=3, workspace_bytes=need, **two)) == 0
+    assert status(fake(T=100, H=3, workspace_bytes=need - 1, **two)) == 7
+    assert status(fake(T=100, H=3, workspace=None, **two)) == 7
+    assert status(fake(T=100, H=3, workspace=0x7F0000000000 + 8 * 256 * MB + 128, **two)) == 7
+    assert kda.kda_prefill_workspace_bytes(fake(T=100, H=3, fuse_prepare=-1)) == need
+    # Fused form: no records, only the status block; with KDA_FLAG_KEEP_RECORDS the
+    # records too.
+    assert kda.kda_prefill_workspace_bytes(fake(T=100, H=3, fuse_prepare=1)) == 256
+    keep = fake(T=100, H=3, fuse_prepare=1, flags=kda.KDA_FLAG_KEEP_RECORDS)
+    assert kda.kda_prefill_workspace_bytes(keep) == 7 * 3 * kda.KDA_WS_RECORD + 256
+    p = kda.kda_prefill_plan(keep)
+    assert p["fused"] == 1 and p["has_records"] == 1 and p["records_offset"] == 0
+    assert p["status_offset"] == 7 * 3 * kda.KDA_WS_RECORD
+    # varlen: (T + 15 N) / 16 chunk records after the 256-byte-rounded header
+    # (cu_chunks, cu_segs, order)
+    v = fake(T=100, H=3, N=5, varlen=True, **two)
+    assert kda.kda_prefill_workspace_bytes(v) == 256 + ((100 + 15 * 5) // 16) * 3 * kda.KDA_WS_RECORD + 256
+    assert kda.kda_prefill_workspace_bytes(fake(T=100, H=3, N=5, varlen=True,
+                                                fuse_prepare=1)) == 256 + 256
 
 
 def test_checkpoint_validation():
@@ -183,7 +196,10 @@ def test_plan_follows_the_slice_rule():
     assert kda.kda_prefill_plan(fake(H=48), 256)["rows_per_workgroup"] == 32
     p = kda.kda_prefill_plan(fake(H=96, T=8192), 256)
     assert p["rows_per_workgroup"] == 64 and p["recurrence_workgroups"] == 192
-    assert p["prepare_workgroups"] == 512 * 96
+    assert p["prepare_workgroups"] == 512 * 96 and p["fused"] == 0
+    f = kda.kda_prefill_plan(fake(H=96, T=8192, fuse_prepare=1), 256)
+    assert f["prepare_workgroups"] == 0 and f["fused"] == 1  # prepared in the recurrence
+    assert f["waves_per_workgroup"] == 4 + 4  # compute waves and producer waves
     # Past one round of 64-row slices, whole heads (BF16 I/O): 8 x 24 pairs.
     v = kda.kda_prefill_plan(fake(H=24, T=20000, N=8, varlen=True), 256)
     assert v["rows_per_workgroup"] == 128 and v["waves_per_workgroup"] == 12
@@ -215,7 +231,11 @@ def test_plan_segments_small_head_counts():
     assert p["scan_transition_offset"] == records + slots * 128 * 128 * 4
     assert p["scan_output_offset"] == records + slots * 128 * 128 * 6
     need = kda.kda_prefill_workspace_bytes(fake(H=6, T=8192))
-    assert need == records + slots * 128 * 128 * 6 + 512 * 6 * 2048 * 2
+    assert need == records + slots * 128 * 128 * 6 + 512 * 6 * 2048 * 2 + 256
+    # the fused form keeps no records: the scan slots come first
+    fp = kda.kda_prefill_plan(fake(H=6, T=8192, fuse_prepare=1), 256)
+    assert fp["scan_state_offset"] == 0 and fp["has_records"] == 0
+    assert kda.kda_prefill_workspace_bytes(fake(H=6, T=8192, fuse_prepare=1)) == need - records
     # With checkpoints every later segment is re-run: 2 (2 P - 3) workgroups per pair in
     # launch A, P = (256 / 12 + 3) / 2 = 12 segments of 43 chunks.
     c = kda.kda_prefill_plan(fake(H=6, T=8192, checkpoint_every=1024), 256)
@@ -239,7 +259,7 @@ def test_plan_segments_small_head_counts():
     # Forced serial, forced length, and no segments for many heads.
     s = kda.kda_prefill_plan(fake(H=6, T=8192, segment_chunks=-1), 256)
     assert s["segment_chunks"] == 0 and s["rows_per_workgroup"] == 16
-    assert kda.kda_prefill_workspace_bytes(fake(H=6, T=8192, segment_chunks=-1)) == records
+    assert kda.kda_prefill_workspace_bytes(fake(H=6, T=8192, segment_chunks=-1)) == records + 256
     f = kda.kda_prefill_plan(fake(H=6, T=8192, segment_chunks=100), 256)
     assert f["segment_chunks"] == 100 and f["segments_per_head_bound"] == 6
     assert kda.kda_prefill_plan(fake(H=96, T=8192), 256)["segment_chunks"] == 0

@@ -190,10 +190,12 @@ def test_workspace_too_small_is_rejected_before_launch():
 
     x = kda_synth.config(1, T=32, H=1)
     d = to_device(x)
-    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
-    with pytest.raises(kda.KdaError) as e:
-        kda.kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], workspace=ws)
-    assert e.value.status == 7
+    for kw in (dict(), dict(fuse_prepare=1)):
+        need = kda.kda_prefill_workspace_bytes(kda.make_args(B=1, T=32, H=1, N=1, **kw))
+        ws = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+        with pytest.raises(kda.KdaError) as e:
+            kda.kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], workspace=ws, **kw)
+        assert e.value.status == 7
 
 
 def test_debug_check_cu_seqlens():

@@ -1,7 +1,10 @@
-"""kda_prepare's per-chunk records vs the oracle's literal chunk quantities.
+"""The prepared per-chunk records vs the oracle's literal chunk quantities, from both
+places the preparation runs: the separate kda_prepare kernel (fuse_prepare < 0) and the
+producer waves of the fused recurrence (which write what they put in the LDS ring to the
+workspace when KDA_FLAG_KEEP_RECORDS is set).
 
-After a call the caller-owned workspace holds one record per (chunk, head) in the layout
-documented in include/kda.h. Each record is decoded here and compared with the folded
+After such a call the caller-owned workspace holds one record per (chunk, head) in the
+layout documented in include/kda.h. Each record is decoded here and compared with the folded
 quantities built from ``oracle.chunk_quantities`` (the page's K_start, Q_start, K_end,
 D_{0:15}, A_kk, A_qk) by the algebra the header states:
 Mb = A_kk Diag(beta), Kn = -Mb K_start^T, Qt = s Q_start^T + A_qk Kn.
@@ -67,21 +70,30 @@ def expected(q, k, g, beta, s):
 TOLS = dict(Kn=1e-2, Qt=1e-2, K_end=1e-2, D=1e-5, Mb=1e-2, A_qk=1e-2)
 
 
-def run_and_check(x, chunks_to_check=None, tols=TOLS):
+MODES = {"separate": dict(fuse_prepare=-1), "fused": dict(fuse_prepare=1, keep_records=True)}
+
+
+def run_and_check(x, mode, chunks_to_check=None, tols=TOLS):
     import torch
 
     import chunkwise_delta_rule_kda_amd as kda
 
     d = to_device(x)
-    args = kda.make_args(B=x.B, T=x.T, H=x.H, N=x.N,
-                         cu_seqlens=d.get("cu_seqlens"))
+    kw = MODES[mode]
+    args = kda.make_args(B=x.B, T=x.T, H=x.H, N=x.N, cu_seqlens=d.get("cu_seqlens"),
+                         fuse_prepare=kw.get("fuse_prepare", 0),
+                         flags=kda.KDA_FLAG_KEEP_RECORDS if kw.get("keep_records") else 0)
     need = kda.kda_prefill_workspace_bytes(args)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     q, k, v, g, beta = (d.pop(n) for n in ("q", "k", "v", "g", "beta"))
-    kda.kda_prefill(q, k, v, g, beta, workspace=ws, **d)
+    kda.kda_prefill(q, k, v, g, beta, workspace=ws, **kw, **d)
     torch.cuda.synchronize()
     wsn = ws.cpu().numpy()
-    header = kda.kda_prefill_plan(args)["workspace_header_bytes"]
+    plan = kda.kda_prefill_plan(args)
+    assert plan["has_records"] == 1 and plan["fused"] == (mode == "fused")
+    header = plan["records_offset"]
+    status = wsn[plan["status_offset"]:plan["status_offset"] + 4].view(np.int32)[0]
+    assert status == 0, status
     max_chunks = (x.N * ((x.T + 15) // 16) if x.cu_seqlens is None
                   else (x.T + 15 * x.N) // 16)
     # Oracle-side inputs after the in-kernel transforms (FP64).
@@ -109,7 +121,7 @@ def run_and_check(x, chunks_to_check=None, tols=TOLS):
                     for n in TOLS:
                         worst[n] = max(worst[n], rel_err(got[n], ref[n]))
             gc += 1
-    print("[prepare] worst relative errors:", {n: f"{e:.2e}" for n, e in worst.items()},
+    print(f"[prepare] {mode} worst relative errors:", {n: f"{e:.2e}" for n, e in worst.items()},
           flush=True)
     for n, e in worst.items():
         assert e <= tols[n], (n, e)
@@ -123,24 +135,29 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def test_prepare_config0_fp32():
-    run_and_check(kda_synth.config(0))
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_prepare_config0_fp32(mode):
+    run_and_check(kda_synth.config(0), mode)
 
 
-def test_prepare_bf16_ragged():
-    run_and_check(kda_synth.config(1, T=93, H=2))
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_prepare_bf16_ragged(mode):
+    run_and_check(kda_synth.config(1, T=93, H=2), mode)
 
 
-def test_prepare_varlen_transforms():
-    run_and_check(kda_synth.config(4, H=2, lengths=[20, 0, 33, 5]))
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_prepare_varlen_transforms(mode):
+    run_and_check(kda_synth.config(4, H=2, lengths=[20, 0, 33, 5]), mode)
 
 
-def test_prepare_floor_decay():
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_prepare_floor_decay(mode):
     # g = -5 everywhere: exp(+-G) spans e^{+-80}, the split-exponent's widest range.
-    run_and_check(kda_synth.stress("floor", T=48, H=1))
+    run_and_check(kda_synth.stress("floor", T=48, H=1), mode)
 
 
-def test_prepare_correlated_keys():
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_prepare_correlated_keys(mode):
     # Identical keys, weak decay, beta 0.5: (I + R)^{-1} has entries up to ~1e1.
-    run_and_check(kda_synth.stress("correlated", T=32, H=1),
+    run_and_check(kda_synth.stress("correlated", T=32, H=1), mode,
                   tols=dict(TOLS, Kn=2e-2, Qt=2e-2, Mb=2e-2))

@@ -64,8 +64,9 @@ def test_no_alloc_rejects_calls_beyond_the_scratch():
     lib = kda.load_library()
     import ctypes
 
-    # H = 12, T = 8192 needs ~120 MB of workspace: rejected before any pointer is used
-    # or any kernel launched (the pointers here are never dereferenced).
+    # H = 12, T = 8192 with the separate preparation kernel needs ~85 MB of records:
+    # rejected before any pointer is used or any kernel launched (the pointers here are
+    # never dereferenced).
     a = kda.make_args(B=1, T=8192, H=12, N=1, q=1 << 20, k=2 << 20, v=3 << 20, g=4 << 20,
                       beta=5 << 20, o=6 << 20)
     assert kda.kda_prefill_workspace_bytes(a) > kda.KDA_NO_ALLOC_SCRATCH_BYTES
