@@ -385,6 +385,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step line")
     ap.add_argument("--no-head-sweep", action="store_true", help="skip the H=24/48 lines")
+    ap.add_argument("--no-fused-lines", action="store_true",
+                    help="skip the fused-form lines (fuse_prepare=1 at H=6/24/96)")
     ap.add_argument("--fuse-prepare", type=int, default=0,
                     help="0 automatic, 1 chunk preparation fused into the recurrence, -1 a "
                          "separate preparation kernel")
@@ -456,12 +458,13 @@ def main():
     main_s["graph_replay_us"] = time_graph(x, args.steps, args.warmup, device)
     progress(f"config{args.config}: {main_s}")
 
-    # Dominant kernel: the recurrence kernel (the serial chain). It runs once per call in
-    # the serial form and in the affine-output segmented form (the first launch: segment
-    # 0 and the zero-start and transition runs of the later segments; the combine and the
-    # scan-output pass are other kernels), which is the form a call without checkpoints
-    # takes. Roofline on the path's algorithmic MFMA work of the recurrence (all token-
-    # heads pass through this launch) per launch duration.
+    # Dominant kernel: the first recurrence launch (the serial chain), the longest launch
+    # of the call. It runs once per call in the serial form and in the affine-output
+    # segmented form (segment 0, and the zero-start and transition runs of the later
+    # segments; the combine and the scan-output pass are other kernels), the form a call
+    # without checkpoints takes. `achieved` charges the path's algorithmic recurrence
+    # FLOP (every token-head passes through this launch) to this launch alone;
+    # `recurrence_all_launches` charges them to the three recurrence launches together.
     launches = 1
     kern_us = statistics.mean(r["rec_a_ms"]) * 1e3
     avg_launch_us = kern_us / launches
@@ -469,12 +472,26 @@ def main():
     rec_flop = th * FLOP_REC_PER_TOKEN_HEAD
     achieved = rec_flop / launches / (avg_launch_us * 1e-6) / 1e12
     workload = f"config{args.config}"
-    roofline = dict(bound="mfma", kernel="kda_recurrence", achieved=round(achieved, 3),
-                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+    phases = main_s["recurrence_phases_us"]
+    rec_all_us = phases["first"] + phases["combine"] + phases["scan_output"]
+    rec_all_tflops = rec_flop / (rec_all_us * 1e-6) / 1e12
+    traffic = traffic_from_profiles("kda_recurrence", workload)
+    traffic_src = (f"profiles/traffic_kda_recurrence_{workload}.txt, FETCH_SIZE + WRITE_SIZE "
+                   f"per launch, counted for kernel_source_hash {kernel_hash()}"
+                   if traffic is not None else None)
+    roofline = dict(bound="mfma", kernel="kda_recurrence (first recurrence launch)",
+                    achieved=round(achieved, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 6),
-                    traffic=traffic_from_profiles("kda_recurrence", workload),
+                    traffic=traffic, traffic_source=traffic_src,
+                    hbm_frac_of_traffic=(round(traffic / (avg_launch_us * 1e-6) /
+                                               (PEAK_HBM_GBS * 1e9), 5)
+                                         if traffic is not None else None),
                     avg_launch_us=round(avg_launch_us, 3), launches_per_call=launches,
-                    flop_per_launch=rec_flop / launches)
+                    flop_per_launch=rec_flop / launches,
+                    recurrence_all_launches=dict(
+                        us=round(rec_all_us, 3), achieved=round(rec_all_tflops, 3),
+                        unit="TFLOP/s",
+                        frac=round(rec_all_tflops / PEAK_BF16_TFLOPS, 6)))
 
     per_config = {workload: main_s}
     for c in [int(c) for c in args.extra_configs.split(",") if c.strip()]:
@@ -510,6 +527,19 @@ def main():
                 xh, time_config(xh, max(5, args.steps // 5), 2, device, hip))
             progress(f"H={hh}: {per_config[f'H{hh}_T8192']}")
             del xh
+            torch.cuda.empty_cache()
+    # The fused form (fuse_prepare=1: each chunk prepared by producer waves of the
+    # recurrence workgroup into its LDS ring, no record through HBM) at H = 6, 24 and 96,
+    # next to the automatic two-kernel form measured above.
+    if not args.no_fused_lines and args.fuse_prepare <= 0:
+        for name, xf in (("fused_H6_T8192", lambda: kda_synth.config(1)),
+                         ("fused_H24_T8192", lambda: kda_synth.config(1, H=24)),
+                         ("fused_H96_T8192", lambda: kda_synth.config(3))):
+            xf = xf()
+            per_config[name] = summarize(
+                xf, time_config(xf, max(5, args.steps // 5), 2, device, hip, fuse_prepare=1))
+            progress(f"{name}: {per_config[name]}")
+            del xf
             torch.cuda.empty_cache()
     # Fractions against the rates measured on this machine as well as the published peaks.
     for v in per_config.values():
