@@ -45,11 +45,16 @@ KERNEL_SOURCES = ["kda_prepare.hip", "kda_recurrence.hip", "kda_fused.hip", "kda
 
 
 def kernel_hash():
+    """Hash of the kernel sources' code: comments and blank space are dropped first, so
+    that a comment edit does not orphan the counter profiles taken of the same code."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "chunkwise_delta_rule_kda_amd", "csrc")
     for n in KERNEL_SOURCES:
-        with open(os.path.join(d, n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(d, n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

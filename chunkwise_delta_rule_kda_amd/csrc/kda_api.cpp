@@ -67,6 +67,10 @@ kda_status check_shape(const kda_prefill_args* a) {
     return fail(KDA_ERR_SHAPE, "bad B=%lld T=%lld H=%lld N=%lld", (long long)a->B,
                 (long long)a->T, (long long)a->H, (long long)a->N);
   if (a->H > 65535) return fail(KDA_ERR_SHAPE, "H=%lld exceeds 65535", (long long)a->H);
+  // Bounds under which every size below is computed without overflow.
+  if (a->B > (int64_t(1) << 31) || a->N > (int64_t(1) << 31) || a->T > (int64_t(1) << 40))
+    return fail(KDA_ERR_SHAPE, "B=%lld N=%lld T=%lld out of range", (long long)a->B,
+                (long long)a->N, (long long)a->T);
   if (a->cu_seqlens) {
     if (a->B != 1) return fail(KDA_ERR_SHAPE, "packed varlen needs B=1 (got %lld)", (long long)a->B);
     if (a->N < 1) return fail(KDA_ERR_SHAPE, "packed varlen needs N>=1");
@@ -77,6 +81,7 @@ kda_status check_shape(const kda_prefill_args* a) {
   const int64_t mc = max_chunks_of(a);
   if (mc > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "too many chunks (%lld)", (long long)mc);
   if (a->N * a->H * 8 > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "N*H too large");
+  if (mc * a->H > (int64_t(1) << 40)) return fail(KDA_ERR_SHAPE, "chunks*H too large");
   if (a->io_dtype != KDA_BF16 && a->io_dtype != KDA_FP32)
     return fail(KDA_ERR_DTYPE, "io_dtype %d", a->io_dtype);
   if (a->state_dtype != KDA_BF16 && a->state_dtype != KDA_FP32)
@@ -98,17 +103,19 @@ kda_status check_shape(const kda_prefill_args* a) {
     return fail(KDA_ERR_CONFIG, "rows_per_workgroup %d", a->rows_per_workgroup);
   if (a->segment_chunks > (1 << 24))
     return fail(KDA_ERR_CONFIG, "segment_chunks %d", a->segment_chunks);
-  if (a->checkpoint_every < 0 || a->checkpoint_every % KDA_CHUNK != 0)
+  if (a->checkpoint_every < 0 || a->checkpoint_every > (int64_t(1) << 40) ||
+      a->checkpoint_every % KDA_CHUNK != 0)
     return fail(KDA_ERR_CONFIG, "checkpoint_every %lld is not a non-negative multiple of 16",
                 (long long)a->checkpoint_every);
-  if (a->checkpoint_rows < 0)
+  if (a->checkpoint_rows < 0 || a->checkpoint_rows > (int64_t(1) << 40))
     return fail(KDA_ERR_CONFIG, "checkpoint_rows %lld", (long long)a->checkpoint_rows);
   if (a->ssm_state_indices) {
     const int64_t dense = a->H * KDA_HEAD_DIM * KDA_HEAD_DIM;
     if (!a->state_in) return fail(KDA_ERR_CONFIG, "a state pool needs state_in");
-    if (a->state_pool_slots < 1)
+    if (a->state_pool_slots < 1 || a->state_pool_slots > (int64_t(1) << 31))
       return fail(KDA_ERR_CONFIG, "state_pool_slots %lld", (long long)a->state_pool_slots);
-    if (a->state_slot_pitch != 0 && (a->state_slot_pitch < dense || a->state_slot_pitch % 8))
+    if (a->state_slot_pitch != 0 && (a->state_slot_pitch < dense || a->state_slot_pitch % 8 ||
+                                     a->state_slot_pitch > (int64_t(1) << 40)))
       return fail(KDA_ERR_CONFIG, "state_slot_pitch %lld", (long long)a->state_slot_pitch);
   }
   return KDA_OK;
@@ -161,9 +168,10 @@ struct Plan {
 // The fused form (producer waves in the recurrence workgroups prepare the chunks) when
 // the caller asks for it. The automatic choice is the separate preparation kernel: on
 // MI355X the fused form's producers (one wave per chunk, about 12k cycles of dependent
-// work each) leave the compute waves waiting, 1.5-2x slower at every head count measured
-// (T = 8192, H = 6: 126 vs 72 us per call; H = 96: 811 vs 634 us), although it moves
-// only the algorithmic bytes.
+// work each) leave the compute waves waiting, 1.5-1.8x slower at every head count
+// measured (T = 8192, warm per call, H = 6: 112 vs 66 us; H = 24: 353 vs 208 us;
+// H = 96: 953 vs 555 us), although it moves only 1.08x the algorithmic bytes at H = 96
+// (the two-kernel form 2.4x).
 bool fused_form(const kda_prefill_args* a) { return a->fuse_prepare > 0; }
 
 // A few tokens per sequence (fixed layout, 1 <= T <= kDecodeMaxT, no checkpoints,

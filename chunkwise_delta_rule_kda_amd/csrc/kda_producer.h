@@ -1,39 +1,38 @@
 // Producer waves of the fused recurrence: the chunk preparation of the "FlashKDA column
 // split" post, section 1 ("FlashKDA in two kernels": K_start, Q_start, K_end, D_{0:15},
 // A_kk = (I + R)^{-1}, A_qk), computed by the recurrence workgroup itself, one chunk per
-// pair of producer waves (each taking 64 of the 128 keys), straight into the LDS ring
-// its compute waves read. The record an LDS
-// slot receives is the folded record of include/kda.h (Mb = A_kk B, Kn = -Mb K_start^T,
-// Qt = s Q_start^T + A_qk Kn, K_end^T, D), in the same lane layout, followed by the
-// chunk's V tile; nothing of it goes through HBM.
+// producer wave (four producer waves take the run's chunks in turn), straight into the
+// LDS ring its compute waves read. The record an LDS slot receives is the folded record
+// of include/kda.h (Mb = A_kk B, Kn = -Mb K_start^T, Qt = s Q_start^T + A_qk Kn, K_end^T,
+// D), in the same lane layout, followed by the chunk's V tile; nothing of it goes
+// through HBM. (kPaired below selects the other arrangement, measured and not taken: two
+// waves per chunk, 64 keys each, exchanging partial sums.)
 //
 // Included by kda_recurrence_core.h inside namespace kda (anonymous namespace), after the
 // Params / Task / MFMA helpers it uses.
 //
 // Lane layout of a producer wave (lane L = 16 grp + m): token m of the chunk, keys
-// kappa(kb, grp, e) = 32 kb + 16 (e / 4) + 4 grp + e % 4 for its two key groups kb (0, 1
-// or 2, 3), e = 0..7 (the record's key order). The 16 tokens of a key set form one 16-lane row, so the prefix of
-// g over the chunk is a DPP row scan and D_{0:15} = exp(G_15) a row broadcast, as in
-// kda_prepare. Then:
+// kappa(kb, grp, e) = 32 kb + 16 (e / 4) + 4 grp + e % 4 for its key groups kb, e = 0..7
+// (the record's key order). The 16 tokens of a key set form one 16-lane row, so the
+// prefix of g over the chunk is a DPP row scan and D_{0:15} = exp(G_15) a row
+// broadcast, as in kda_prepare. Then:
 // - R and A_qk are 16x16x32 MFMA products over the keys, with the scaled rows as
 //   operands straight from registers (the K3 decay page's split-exponent form: decayed
 //   key rows exp(G_i) k_i against exp(-G_j) k_j, safe because g >= -5 keeps |G| <= 80);
-//   each wave of a pair sums its 64 keys and the two partial sums are exchanged through
-//   LDS, so both hold the whole of R and A_qk;
 // - (I + R)^{-1} is a 16-step forward substitution in FP32 over 16 lanes (one column
 //   each) with R's rows broadcast from a 1 KB LDS scratch, and P = A_qk Mb four FP32
-//   16x16x4 MFMA products (with pairs, both waves do this rather than exchange it);
+//   16x16x4 MFMA products;
 // - the key-major tiles the record needs (K_start^T as an MFMA operand, K_end^T) are
 //   16x16 transposes done by a 16x16x16 MFMA against the identity in the operands' own
 //   k order: exact (one BF16 term per output) and independent of how the hardware
 //   assigns k to lanes;
 // - Kn^T and Qt^T are 16x16x16 MFMA products, as in kda_prepare.
 //
-// Synchronisation is by counters in LDS, not by the workgroup barrier: the two waves of a
-// pair meet once per chunk to exchange partial sums (pair[]); each of them waits until
-// every compute wave has read the slot's previous chunk (done[s] counts reads), writes its
-// half of the slot, waits for its writes and adds one to ready[s]; a compute wave waits
-// until ready[s] counts both halves of its chunk, reads, and adds to done.
+// Synchronisation is by counters in LDS, not by the workgroup barrier: a producer waits
+// until every compute wave has read the slot's previous chunk (done[s] counts reads),
+// writes the slot, waits for its writes and adds two to ready[s] (one per half of the
+// slot, the count a pair of waves would reach); a compute wave waits until ready[s]
+// counts both halves of its chunk, reads, and adds to done.
 // Every wait is bounded: past kSpinLimit polls the wave sets the workgroup's abort flag
 // and the call's status word (a device int the host can read) and every wave of the
 // workgroup leaves its loop, so the kernel always ends.
@@ -44,8 +43,9 @@ namespace fused {
 // Keys a producer wave covers: all 128 (kPaired false: one wave per chunk, one producer
 // per SIMD, up to 256 registers) or 64 (kPaired true: two waves per chunk exchanging
 // partial sums, two producers per SIMD next to each compute wave, at most 168 registers).
-// Measured at T = 8192 (H = 96, serial form, 64-row workgroups): one wave per chunk
-// 811 us, pairs 1192 us.
+// Measured at T = 8192 (H = 96, serial form, 64-row workgroups) with an earlier state of
+// the producer code: one wave per chunk 811 us, pairs 1192 us (the one-wave form as it
+// stands takes about 970 us).
 constexpr bool kPaired = false;
 constexpr int producers(int w) { return kPaired && w < 8 ? 8 : 4; }
 constexpr int kHalvesPerWave = kPaired ? 1 : 2;

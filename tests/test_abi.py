@@ -93,6 +93,10 @@ def test_null_required_pointer(field):
     (dict(io_dtype=7), 3), (dict(state_dtype=-1), 3),
     (dict(flags=1 << 5), 4), (dict(rows_per_workgroup=24), 10),
     (dict(scale=float("nan")), 5),
+    # sizes bounded before any arithmetic on them (no signed overflow)
+    (dict(T=(1 << 40) + 1), 2), (dict(T=(1 << 63) - 1), 2), (dict(B=(1 << 31) + 1), 2),
+    (dict(H=4096, T=1 << 30, B=1 << 8, N=1 << 8), 2),
+    (dict(checkpoint_every=1 << 41), 10), (dict(checkpoint_every=16, checkpoint_rows=1 << 41), 10),
 ])
 def test_shape_dtype_flag_rejections(kw, code):
     assert status(fake(**kw)) == code
