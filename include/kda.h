@@ -213,7 +213,11 @@ typedef struct kda_prefill_args {
      (the prepared records never go through HBM). 0 (automatic) or negative: a separate
      preparation kernel (one workgroup per chunk and head) writes the records to the
      workspace first and the recurrence streams them back. Results differ only by
-     rounding. */
+     rounding. The fused form is this library's take on the producer / consumer overlap
+     of the "CAKE KDA Prefill" page (sections "Owner-helper decomposition" and
+     "Fine-grained K1-K2 overlap"); it moves about 1x the algorithmic HBM bytes instead
+     of about 2.4x, but on MI355X its producers are slower than the separate kernel at
+     every head count measured, which is why it is not the automatic choice. */
   int32_t fuse_prepare;
 } kda_prefill_args;
 
