@@ -71,5 +71,22 @@ def build(verbose=False, out=LIB, extra_flags=(), jobs=None):
     return out
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_caller", "kda_c_caller.c")
+C_CALLER = os.path.join(ROOT, "tests", "c_caller", "kda_c_caller")
+
+
+def build_c_caller(verbose=False):
+    """The C client used by the tests (plain C against include/kda.h and the HIP runtime,
+    linked to the in-tree libkda.so)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           C_CALLER_SRC, "-o", C_CALLER, "-L", PKG, "-lkda", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../chunkwise_delta_rule_kda_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    _run(cmd, "the C client", verbose)
+    return C_CALLER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
