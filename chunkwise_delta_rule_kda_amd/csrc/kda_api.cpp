@@ -393,8 +393,12 @@ kda_status kda_prefill_check(const kda_prefill_args* a) {
       return fail(KDA_ERR_WORKSPACE, "workspace not 256-byte aligned");
   }
   const bool ckpt = a->checkpoint_every > 0;
-  if (ckpt && (!a->state_checkpoints || !a->checkpoint_cu_starts))
-    return fail(KDA_ERR_NULL, "checkpoints need state_checkpoints and checkpoint_cu_starts");
+  // With no checkpoint rows nothing is ever written, so state_checkpoints may be NULL
+  // (the data pointer of a zero-size buffer often is); the row offsets are still read.
+  if (ckpt && !a->checkpoint_cu_starts)
+    return fail(KDA_ERR_NULL, "checkpoints need checkpoint_cu_starts");
+  if (ckpt && a->checkpoint_rows > 0 && !a->state_checkpoints)
+    return fail(KDA_ERR_NULL, "checkpoint_rows > 0 needs state_checkpoints");
   // Alignment the kernels' vector accesses rely on.
   const void* vec[] = {a->q, a->k, a->v, a->g, a->o, a->state_in, a->state_out,
                        ckpt ? a->state_checkpoints : nullptr};

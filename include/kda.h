@@ -164,7 +164,8 @@ typedef struct kda_prefill_args {
      r * checkpoint_every tokens of the sequence (r = 0: its initial state). An empty
      sequence writes none.
      state_checkpoints: [checkpoint_rows, H, 128 (values), 128 (keys)] of state_dtype,
-     device, 16-byte aligned, write only, must not overlap any other buffer.
+     device, 16-byte aligned, write only, must not overlap any other buffer; it may be
+     NULL when checkpoint_rows is 0 (nothing is written then).
      checkpoint_cu_starts: int64 [N + 1] device, the caller's row offsets (on the page's
      contract, cu[0] = 0 and cu[n + 1] - cu[n] = ceil(len_n / checkpoint_every); they
      are device data and not checked on the host). Rows at or beyond checkpoint_rows are

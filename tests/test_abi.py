@@ -163,6 +163,11 @@ def test_checkpoint_validation():
     assert status(fake(**dict(ck, checkpoint_every=-16))) == 10
     assert status(fake(**dict(ck, checkpoint_rows=-1))) == 10
     assert status(fake(**dict(ck, state_checkpoints=None))) == 1
+    # No rows: nothing is written, so a NULL buffer (a zero-size tensor's pointer) is fine;
+    # the row offsets are still required.
+    assert status(fake(**dict(ck, checkpoint_rows=0, state_checkpoints=None))) == 0
+    assert status(fake(**dict(ck, checkpoint_rows=0, state_checkpoints=None,
+                              checkpoint_cu_starts=None))) == 1
     assert status(fake(**dict(ck, checkpoint_cu_starts=None))) == 1
     assert status(fake(**dict(ck, state_checkpoints=base + 10 * 256 * MB + 8))) == 2
     assert status(fake(**dict(ck, state_checkpoints=base + 2 * 256 * MB))) == 6   # == v

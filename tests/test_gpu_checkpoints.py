@@ -117,3 +117,17 @@ def test_rows_beyond_the_buffer_are_not_written():
     assert ck.data_ptr() == big.data_ptr()
     assert torch.all(big[5:] == 7.0)
     assert not torch.all(big[:5] == 7.0)
+
+
+@pytest.mark.parametrize("lens", [[0], [0, 0, 0]])
+@pytest.mark.parametrize("L", [-1, 2])
+def test_every_sequence_empty(lens, L):
+    # No token at all: zero checkpoint rows (a zero-size buffer, whose pointer may be
+    # NULL), no output, and each final state is its initial state.
+    x = kda_synth.config(4, H=2, lengths=lens)
+    print(f"[case] all empty {lens} L={L}", flush=True)
+    o, s, raw = run_gpu(x, checkpoint_every=16, segment_chunks=L)
+    assert o.size == 0 and raw[2].shape[0] == 0
+    s0 = (np.zeros((x.N, x.H, 128, 128)) if x.state0 is None
+          else np.asarray(x.state0, np.float64))
+    assert np.array_equal(s, s0)
