@@ -8,6 +8,8 @@ Default workload: T = 8192 tokens, H = 6 heads, d = 128, BF16 (one GPU's share o
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu-baseline]
                     [--extra-configs 2,3] [--calib-copy-mib 1024]
 
+Each timed pass follows an untimed warm-up of at least W calls and at least 100 ms
+(--warmup-ms) of them, so that the GPU clocks have reached their sustained-load rate.
 The step time comes from the timed calls alone. Per-kernel durations come from a second
 pass in which the library records HIP events between its launches on the call's stream;
 the stream time of one event record (measured in the same run) is subtracted from each.
@@ -146,6 +148,30 @@ def make_call(x, device, **extra):
     return call, (o, st)
 
 
+# GPU clocks ramp up under sustained load: after an idle pause, back-to-back calls take
+# about 20-25 ms to reach their steady rate (H=6: 77 -> 71 us per call, H=96: 645 -> 558 us,
+# events between calls). The untimed warm-up therefore runs for at least this long, and
+# for at least the requested number of calls.
+WARMUP_MIN_S = 0.1
+
+
+def warm_up(fn, warmup, min_s=None):
+    """Untimed calls of fn: at least `warmup` of them and at least `min_s` seconds of
+    them (the host waits for the GPU every few calls); returns the number made."""
+    import torch
+
+    min_s = WARMUP_MIN_S if min_s is None else min_s
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < min_s:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def time_graph(x, steps, warmup, device):
     """Microseconds per call when one kda_prefill call is captured in a HIP graph and the
     graph is replayed back to back (the capture semantics are covered by the graph tests)."""
@@ -162,9 +188,7 @@ def time_graph(x, steps, warmup, device):
     with torch.cuda.graph(graph):
         call()
     torch.cuda.synchronize()
-    for _ in range(warmup):
-        graph.replay()
-    torch.cuda.synchronize()
+    warm_up(graph.replay, warmup)
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0.record()
     for _ in range(steps):
@@ -188,9 +212,7 @@ def time_config(x, steps, warmup, device, hip, **extra):
     import torch
 
     call, _ = make_call(x, device, **extra)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
+    progress(f"warm-up: {warm_up(call, warmup)} calls")
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
@@ -381,10 +403,15 @@ def summarize(x, r):
 
 
 def main():
+    global WARMUP_MIN_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed calls before each timed pass (the warm-up also lasts at "
+                         "least --warmup-ms)")
+    ap.add_argument("--warmup-ms", type=float, default=1e3 * WARMUP_MIN_S,
+                    help="minimum duration of each untimed warm-up (clock ramp)")
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--extra-configs", default="0,2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -399,6 +426,7 @@ def main():
                     help="run a plain device copy of this many MiB first (counter "
                          "calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
+    WARMUP_MIN_S = max(0.0, args.warmup_ms) / 1e3
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the KDA prefill path has no multi-GPU "
@@ -578,6 +606,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_ms": round(1e3 * WARMUP_MIN_S, 1),
         "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -1,9 +1,10 @@
 """A seeded sweep of valid random shapes vs the FP64 oracle: every path the library picks
-(token loop, serial, both segmented forms, varlen with transforms) at sizes the oracle
-finishes in well under a second, with forced and automatic geometry. Each case draws,
-from its own seed: the layout (fixed batch or packed varlen with empty and ragged
-sequences), T or the lengths, H, the I/O precision, an initial state or none, the
-recurrence geometry (automatic, or explicit rows and segment length) and, for some,
+(token loop, serial, both segmented forms, the fused form, varlen with transforms) at
+sizes the oracle finishes in well under a second, with forced and automatic geometry.
+Each case draws, from its own seed: the layout (fixed batch or packed varlen with empty
+and ragged sequences), T or the lengths, H, the I/O precision, an initial state or none,
+the recurrence geometry (automatic, or explicit rows and segment length), for some the
+fused form (chunk preparation inside the recurrence workgroups) and, for some,
 checkpoints. Bound: max|err| / max|ref| <= 2e-2 for o, the final state and the
 checkpoints."""
 
@@ -16,7 +17,7 @@ from kda_testlib import rel_err, run_gpu, run_oracle
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
-CASES = 32
+CASES = 128
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -58,6 +59,8 @@ def draw(seed):
     elif geo < 0.55:
         kw["segment_chunks"] = -1
         kw["rows_per_workgroup"] = int(rng.choice([16, 32, 64, 128]))
+    if rng.random() < 0.3:
+        kw["fuse_prepare"] = 1
     if rng.random() < 0.2:
         kw["checkpoint_every"] = int(rng.choice([16, 32, 64]))
     return x, kw
