@@ -204,7 +204,8 @@ def time_config(x, steps, warmup, device, hip, **extra):
     """Three passes over `steps` calls each:
     1. untimed-inside: the calls back to back between two events (the step time);
     2. traced: the library records five events per call between its launches, giving
-       the prepare / first recurrence launch / combine / last launch (scan output)
+       the prepare / first recurrence launch / combine / last launch (carry and output,
+       or the re-run)
        durations;
     3. calibration: two events recorded back to back, `steps` times. Each traced phase
        spans exactly one event record (its start marker), whose stream time is this
@@ -396,7 +397,7 @@ def summarize(x, r):
         recurrence_phases_us=dict(
             first=round(statistics.mean(r["rec_a_ms"]) * 1e3, 2),
             combine=round(statistics.mean(r["combine_ms"]) * 1e3, 2),
-            scan_output=round(statistics.mean(r["rec_c_ms"]) * 1e3, 2)),
+            last=round(statistics.mean(r["rec_c_ms"]) * 1e3, 2)),
         event_marker_us=round(r["event_gap_ms"] * 1e3, 2),
         per_call_us=r["per_call_us"],
     )
@@ -494,10 +495,10 @@ def main():
     # Dominant kernel: the first recurrence launch (the serial chain), the longest launch
     # of the call. It runs once per call in the serial form and in the affine-output
     # segmented form (segment 0, and the zero-start and transition runs of the later
-    # segments; the combine and the scan-output pass are other kernels), the form a call
-    # without checkpoints takes. `achieved` charges the path's algorithmic recurrence
-    # FLOP (every token-head passes through this launch) to this launch alone;
-    # `recurrence_all_launches` charges them to the three recurrence launches together.
+    # segments; the carry-and-output pass is another kernel), the form a call without
+    # checkpoints takes. `achieved` charges the path's algorithmic recurrence FLOP (every
+    # token-head passes through this launch) to this launch alone;
+    # `recurrence_all_launches` charges them to all recurrence launches together.
     launches = 1
     kern_us = statistics.mean(r["rec_a_ms"]) * 1e3
     avg_launch_us = kern_us / launches
@@ -506,7 +507,7 @@ def main():
     achieved = rec_flop / launches / (avg_launch_us * 1e-6) / 1e12
     workload = f"config{args.config}"
     phases = main_s["recurrence_phases_us"]
-    rec_all_us = phases["first"] + phases["combine"] + phases["scan_output"]
+    rec_all_us = phases["first"] + phases["combine"] + phases["last"]
     rec_all_tflops = rec_flop / (rec_all_us * 1e-6) / 1e12
     traffic = traffic_from_profiles("kda_recurrence", workload)
     traffic_src = (f"profiles/traffic_kda_recurrence_{workload}.txt, FETCH_SIZE + WRITE_SIZE "

@@ -143,6 +143,10 @@ int rows_per_wg(const kda_prefill_args* a, int num_cus) {
   return 128;
 }
 
+// Later segments per sequence from which the affine-output form uses the
+// carry-and-output launch (see make_plan).
+constexpr int64_t kCarryMinLater = 6;
+
 // Compute units the automatic segment rule is tuned for (MI355X). The rule must not
 // depend on the device so that the workspace size is a pure function of the arguments.
 constexpr int64_t kScanTargetCUs = 256;
@@ -159,6 +163,7 @@ struct Plan {
   size_t scan_phi = 0;       // offset of the BF16 transitions
   bool affine = false;       // affine-output segmented form (no checkpoints)
   size_t scan_q = 0;         // offset of Qt Phi^T per chunk (affine-output form)
+  bool carry = false;        // affine-output form with the carry-and-output launch
   bool fused = false;        // the recurrence prepares its own chunks (no prepare kernel)
   bool has_records = false;  // the workspace holds the records
   size_t status = 0;         // offset of the 256-byte status block
@@ -253,6 +258,12 @@ Plan make_plan(const kda_prefill_args* a) {
     pl.scan_phi = pl.scan_s + slots * kda::kD * kda::kD * 4;
     end = pl.scan_phi + slots * kda::kD * kda::kD * 2;
     pl.affine = a->checkpoint_every == 0;
+    // Many segments per sequence (few heads): one carry-and-output launch in place of the
+    // combine and the scan output. Measured at T = 8192 (BF16, per call): H = 6 (10 later
+    // segments) 65.1 against 69.1 us; H = 12 (4) 117.5 against 117.3 us; H = 24 and
+    // H = 48 (2) 207.0 against 204.6 us and 397 against 381 us, where the long segments
+    // stream their output terms faster through the scan output's many small workgroups.
+    pl.carry = pl.affine && !a->cu_seqlens && pl.segs_per_seq - 1 >= kCarryMinLater;
     if (pl.affine) {
       pl.scan_q = round_up(end, 256);
       end = pl.scan_q + static_cast<size_t>(pl.max_chunks) * static_cast<size_t>(a->H) * 2048 *
@@ -285,6 +296,11 @@ int64_t scan_out_workgroups(const kda_prefill_args* a, const Plan& pl) {
   const int64_t groups = (pl.seg_len + kda::kScanOutChunks - 1) / kda::kScanOutChunks;
   if (a->cu_seqlens) return a->H * pl.seg_stride * groups;
   return a->H * a->N * (pl.segs_per_seq - 1) * groups;
+}
+
+// Workgroups of the carry-and-output launch: four 32-row blocks per later segment.
+int64_t carry_out_workgroups(const kda_prefill_args* a, const Plan& pl) {
+  return a->H * a->N * (pl.segs_per_seq - 1) * 4;
 }
 
 int64_t scan_c_workgroups(const kda_prefill_args* a, const Plan& pl, int rows) {
@@ -461,9 +477,10 @@ kda_status kda_prefill_plan(const kda_prefill_args* a, int32_t num_cus, kda_plan
   out->segments_per_head_bound = pl.seg_stride;
   if (pl.seg_len > 0) {
     out->recurrence_workgroups = scan_a_workgroups(a, pl, rows);
-    out->scan_c_workgroups =
-        pl.affine ? scan_out_workgroups(a, pl) : scan_c_workgroups(a, pl, rows);
-    out->combine_workgroups = (a->H * a->N + 7) / 8 * 64;
+    out->scan_c_workgroups = pl.carry    ? carry_out_workgroups(a, pl)
+                             : pl.affine ? scan_out_workgroups(a, pl)
+                                         : scan_c_workgroups(a, pl, rows);
+    out->combine_workgroups = pl.carry ? 0 : (a->H * a->N + 7) / 8 * 64;
     out->scan_affine_output = pl.affine ? 1 : 0;
     out->scan_output_offset = pl.scan_q;
   } else {
@@ -596,12 +613,16 @@ kda_status kda_prefill(const kda_prefill_args* a, void* stream_) {
     p.blocks = 2 * KDA_HEAD_DIM / rows;
     if (e == hipSuccess) e = recurrence(scan_a_workgroups(a, pl, rows));
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[3], stream);
-    if (e == hipSuccess && (a->cu_seqlens || pl.segs_per_seq >= (pl.affine ? 2 : 3)))
+    if (e == hipSuccess && !pl.carry &&
+        (a->cu_seqlens || pl.segs_per_seq >= (pl.affine ? 2 : 3)))
       e = kda::launch_combine(p, st_bf16, stream);
     if (e == hipSuccess && ev5) e = hipEventRecord(ev[4], stream);
     p.mode = kda::kModeScanC;
     p.blocks = KDA_HEAD_DIM / rows;
-    if (pl.affine) {
+    if (pl.carry) {
+      if (e == hipSuccess)
+        e = kda::launch_carry_out(p, carry_out_workgroups(a, pl), io_bf16, st_bf16, stream);
+    } else if (pl.affine) {
       if (e == hipSuccess) e = kda::launch_scan_output(p, scan_out_workgroups(a, pl), io_bf16, stream);
     } else {
       if (e == hipSuccess) e = recurrence(scan_c_workgroups(a, pl, rows));

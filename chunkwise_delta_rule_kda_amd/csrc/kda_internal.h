@@ -103,6 +103,11 @@ hipError_t launch_fused_recurrence(const Params& p, int64_t workgroups, bool io_
 hipError_t launch_combine(const Params& p, bool state_bf16, hipStream_t stream);
 hipError_t launch_scan_output(const Params& p, int64_t workgroups, bool io_bf16,
                               hipStream_t stream);
+// The affine-output form's last launch when it replaces the combine and the scan output
+// (fixed layout): start states by the chain of transitions, then the output term of
+// every later segment, and the final state (kda_recurrence.hip).
+hipError_t launch_carry_out(const Params& p, int64_t workgroups, bool io_bf16, bool state_bf16,
+                            hipStream_t stream);
 hipError_t launch_decode(const Params& p, bool io_bf16, bool state_bf16, hipStream_t stream);
 
 }  // namespace kda

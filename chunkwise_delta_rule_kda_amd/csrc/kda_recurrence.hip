@@ -33,6 +33,9 @@
 //      giving the final state;
 //   C: o += (Qt Phi^T) S_p^T for every chunk of segments 1..P-1, in parallel
 //      (kda_scan_output_kernel).
+// With many segments per sequence B and C are replaced by one launch
+// (kda_carry_out_kernel) in which every later segment forms its own start state from
+// S_1 by the chain of B and then adds its output term.
 // Calls with state checkpoints need the states inside the later segments and take the
 // re-run form instead: A computes Z_p and Phi_p of segments 1..P-2 only, B stops at
 // S_{P-1}, and C runs segments 1..P-1 again from S_p with this kernel, writing O, the
@@ -360,6 +363,233 @@ __global__ __launch_bounds__(256, BF16IO ? 4 : 2) void kda_scan_output_kernel(Pa
   }
 }
 
+// Carry-and-output launch: the affine-output form's alternative to the combine and
+// scan-output launches for sequences cut into many segments (the small-head regime).
+// S_p follows from segment 0's end state S_1 by S_{s+1} = S_s Phi_s + Z_s; one
+// workgroup per (head, later segment p, block of 32 value rows) forms S_p for its rows
+// by that chain of p - 1 steps, then adds (Qt_c Phi_{p,c}^T) S_p^T to o for every chunk
+// c of segment p (the scan-output term); the last segment's workgroups take one more
+// step, to the final state. Each workgroup repeats the chain prefix of the segments
+// before its own, so no workgroup waits for another one and there is no combine launch
+// in between: the segments with short chains stream their outputs while the long
+// chains still run.
+// Chain step: wave w computes output key blocks 2 w and 2 w + 1 of both row blocks
+// (sixteen 16x16x32 products) with its 32-key slice of Phi_s^T as the A operand and the
+// packed state, exchanged through LDS, as the B operand; Z_s is added in FP32. The step
+// time is set by the operand stream (32 KB of Phi and 16 KB of Z per step), so those
+// loads run kCarryDepth steps ahead. Output: wave w takes chunks c0 + w, c0 + w + 4,
+// ...; the loads of its first kCarryOut chunks do not depend on the chain and are issued
+// right after the chain's first operands (loads retire in order, so the chain's first
+// waits do not include them), then each chunk kCarryOut ahead.
+constexpr int kCarryDepth = 2;  // chain steps of Phi and Z in flight per wave
+
+struct CarryIn {
+  u32x4 a[2][4];  // Phi^T operands: output key block 2 w + i, input key group kk
+  f32x4 z[2][2];  // Z rows 16 (R0 + r) + m, keys 16 (2 w + i) + 4 grp + j
+};
+
+// Output chunks in flight per wave (an FP32 chunk holds twice the registers).
+template <bool BF16IO>
+constexpr int carry_out_depth() { return BF16IO ? 4 : 2; }
+
+template <bool BF16IO, bool BF16ST>
+__global__ __launch_bounds__(256, 1) void kda_carry_out_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) unsigned char xch_[2 * 2 * 4 * 64 * 16];
+  lds_u8* xbase = (lds_u8*)(xch_);  // address-space cast
+  // Tasks (head, sequence, later segment, 32-row block), row blocks fastest: the four
+  // row blocks of one segment, which read the same Phi, Z slots and Qt Phi^T, run on one
+  // XCD. Fixed layout only.
+  const int64_t task = task_index();
+  const int64_t later = p.segs_per_seq - 1;
+  const int64_t per_head = p.N * later * 4;
+  if (per_head <= 0) return;
+  const int64_t h = task / per_head;
+  if (h >= p.H) return;
+  const int64_t rem = task - h * per_head;
+  const int rb = static_cast<int>(rem & 3);
+  const int64_t n = (rem >> 2) / later;
+  const int64_t seg = 1 + ((rem >> 2) - n * later);
+  const int64_t first = n * p.segs_per_seq;
+  const int64_t nseg = p.segs_per_seq;
+  const bool fin = seg == nseg - 1 && p.state_out;  // also forms the final state S_P
+  const int64_t lastf = fin ? seg : seg - 1;         // chain steps s = 1 .. lastf
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int m = lane & 15;
+  const int grp = lane >> 4;
+  const int R0 = 2 * rb;  // first 16-row block of the workgroup
+
+  // ---- the chain's first operands: S_1 and the first kCarryDepth steps --------------
+  const int64_t slot0 = h * p.seg_stride + first;
+  const float* sbase = p.scan_s + slot0 * (kD * kD);
+  const unsigned char* pbase =
+      reinterpret_cast<const unsigned char*>(p.scan_phi + slot0 * (kD * kD));
+  const int aoff = (2 * wave * 4 * 64 + lane) * 16;  // bytes: block 2 wave, group 0
+  int64_t koff[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) koff[r][i] = state_frag(R0 + r, 2 * wave + i, lane);
+  auto fetch = [&](CarryIn& x, int64_t s) {
+    s = s < lastf ? s : lastf;  // past the last step: re-read it (in bounds, unused)
+    const unsigned char* ph = pbase + s * (kD * kD * 2) + aoff;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        x.a[i][kk] = *reinterpret_cast<const u32x4*>(ph + (i * 4 + kk) * 1024);
+    // Z_s lives in slot s + 1; the last segment's in the sequence's first slot.
+    const float* z = sbase + (s + 1 < nseg ? s + 1 : 0) * (kD * kD);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) x.z[r][i] = load4<false>(z, koff[r][i]);
+  };
+  f32x4 st[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st[r][i] = load4<false>(sbase + kD * kD, koff[r][i]);  // S_1
+  CarryIn in[kCarryDepth];
+  if (lastf >= 1) {
+#pragma unroll
+    for (int d = 0; d < kCarryDepth; ++d) fetch(in[d], 1 + d);
+  }
+
+  // ---- this wave's first output chunks (independent of the chain) ---------------------
+  int64_t start, end, chunk0, nch;
+  seq_range(p, n, start, end, chunk0, nch);
+  const int64_t c0 = seg * p.seg_len;
+  const int64_t c1 = min(c0 + p.seg_len, nch);
+  const int64_t nj = c1 - c0 > wave ? (c1 - c0 - wave + 3) / 4 : 0;  // this wave's chunks
+  const int64_t vstride = p.H * kD;
+  const int64_t qbase = (h * p.max_chunks + chunk0) * (4 * 64 * 8) + lane * 8;
+  const int64_t ocol = h * kD + 32 * rb + 4 * grp;
+  // Element offset of O[token tm of chunk c][values 16 (R0 + r) + 4 grp + j].
+  auto oidx = [&](int64_t c, int tm, int r) {
+    return (start + c * kC + tm) * vstride + ocol + 16 * r;
+  };
+  constexpr int kCarryOut = carry_out_depth<BF16IO>();
+  ScanOutIn<BF16IO> ob[kCarryOut];
+  int64_t jn = 0;  // next of this wave's chunks to load; past the last, re-read the last
+  auto issue = [&](ScanOutIn<BF16IO>& x) {
+    const int64_t c = c0 + wave + 4 * (jn < nj ? jn : nj - 1);
+    const int64_t valid = end - (start + c * kC);
+    const int tm = m < valid ? m : static_cast<int>(valid) - 1;  // stay in the sequence
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      x.q[kb] = load_frag<BF16IO>(p.scan_q, qbase + c * (4 * 64 * 8) + kb * 64 * 8);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if constexpr (BF16IO)
+        x.oz[r] = *reinterpret_cast<const u32x2*>(static_cast<const unsigned short*>(p.o) +
+                                                  oidx(c, tm, r));
+      else
+        x.oz[r] = load4<false>(p.o, oidx(c, tm, r));
+    }
+    ++jn;
+  };
+  if (nj > 0) {
+#pragma unroll
+    for (int d = 0; d < kCarryOut; ++d) issue(ob[d]);
+  }
+
+  // ---- the chain S_1 -> S_p (-> S_P) --------------------------------------------------
+  // [parity 2][row block r 2][wave 4][lane 64]: packed S^T key blocks 2 w, 2 w + 1
+  auto xch = [&](int parity, int r, int w) {
+    return reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
+        xbase + ((parity * 2 + r) * 4 + w) * 1024 + lane * 16);
+  };
+#pragma unroll
+  for (int r = 0; r < 2; ++r) *xch(1, r, wave) = pack8(st[r][0], st[r][1]);
+  lds_barrier();
+  // Step s: S_{s+1} = S_s Phi_s + Z_s with operands in set (s - 1) % depth; the set is
+  // then refilled with step s + depth. Whole groups of depth steps are unrolled without
+  // conditions so that the compiler's wait before each step is for its own set only.
+  auto step = [&](auto set_c, int64_t s) {
+    constexpr int set = decltype(set_c)::value;
+    bf16x8 sp[2][4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sp[r][kk] = *xch(s & 1, r, kk);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f32x4 acc = zero;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc = mfma32(__builtin_bit_cast(bf16x8, in[set].a[i][kk]), sp[r][kk], acc);
+        st[r][i] = acc + in[set].z[r][i];
+      }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) *xch((s + 1) & 1, r, wave) = pack8(st[r][0], st[r][1]);
+    fetch(in[set], s + kCarryDepth);
+    lds_barrier();
+  };
+  int64_t s = 1;
+#pragma unroll 1
+  for (; s + kCarryDepth - 1 <= lastf; s += kCarryDepth)
+    unroll<kCarryDepth>([&](auto d) { step(d, s + decltype(d)::value); });
+  unroll<kCarryDepth - 1>([&](auto d) {
+    if (s + decltype(d)::value <= lastf) step(d, s + decltype(d)::value);
+  });
+  // S_p (parity p & 1; a final step wrote the other parity) as A operands: key group kb
+  // of row block r is wave kb's packed piece.
+  bf16x8 sa[2][4];
+  const int par = static_cast<int>(seg & 1);
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sa[r][kb] = *xch(par, r, kb);
+  if (fin) {  // st holds S_P
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int64_t srow = state_row(p, n, h, 16 * (R0 + r) + m);
+      if (srow < 0) continue;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        store4<BF16ST>(p.state_out, srow + 16 * (2 * wave + i) + 4 * grp, st[r][i]);
+    }
+  }
+
+  // ---- output: o += (Qt Phi^T) S_p^T for this wave's chunks ---------------------------
+  if (nj <= 0) return;  // no barrier follows
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  auto body = [&](auto d_c, int64_t j) {
+    constexpr int d = decltype(d_c)::value;
+    const int64_t c = c0 + wave + 4 * j;
+    const bool tv = m < end - (start + c * kC);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      f32x4 acc = mfma32(sa[r][0], ob[d].q[0], zero);
+      acc = mfma32(sa[r][1], ob[d].q[1], acc);
+      acc = mfma32(sa[r][2], ob[d].q[2], acc);
+      acc = mfma32(sa[r][3], ob[d].q[3], acc);
+      f32x4 oz;
+      if constexpr (BF16IO) {
+        const u32x2 w = ob[d].oz[r];
+        oz = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                   __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+      } else {
+        oz = ob[d].oz[r];
+      }
+      if (tv) store4<BF16IO>(p.o, oidx(c, m, r), acc + oz);
+    }
+    issue(ob[d]);
+  };
+  int64_t j = 0;
+#pragma unroll 1
+  for (; j + kCarryOut <= nj; j += kCarryOut)
+    unroll<kCarryOut>([&](auto d) { body(d, j + decltype(d)::value); });
+  unroll<kCarryOut - 1>([&](auto d) {
+    if (j + decltype(d)::value < nj) body(d, j + decltype(d)::value);
+  });
+}
+
 template <bool BF16IO, bool BF16ST, bool CK>
 void launch_waves(const Params& p, dim3 grid, hipStream_t stream) {
   switch (p.waves) {
@@ -418,6 +648,22 @@ hipError_t launch_scan_output(const Params& p, int64_t workgroups, bool io_bf16,
   const dim3 grid(static_cast<unsigned>(workgroups));
   if (io_bf16) hipLaunchKernelGGL(kda_scan_output_kernel<true>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(kda_scan_output_kernel<false>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_carry_out(const Params& p, int64_t workgroups, bool io_bf16, bool state_bf16,
+                            hipStream_t stream) {
+  if (workgroups <= 0) return hipSuccess;
+  workgroups = (workgroups + 7) / 8 * 8;  // whole XCD rounds (see task_index)
+  if (workgroups > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(workgroups));
+  if (io_bf16) {
+    if (state_bf16) hipLaunchKernelGGL((kda_carry_out_kernel<true, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((kda_carry_out_kernel<true, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (state_bf16) hipLaunchKernelGGL((kda_carry_out_kernel<false, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((kda_carry_out_kernel<false, false>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -203,7 +203,8 @@ typedef struct kda_prefill_args {
      trace_events[2] after the last recurrence kernel, all on the call's stream. When
      n_trace_events >= 5 it also records trace_events[3] after the first recurrence
      launch and trace_events[4] after the segment combine (both right after the
-     recurrence in the serial form). */
+     recurrence in the serial form; trace_events[4] right after trace_events[3] when
+     the carry-and-output launch replaces the combine). */
   void *const *trace_events;
   int32_t n_trace_events;
 
@@ -246,10 +247,16 @@ typedef struct kda_prefill_args {
  *                                 segment, S = segments_per_head_bound; inside a slot,
  *                                 MFMA fragments [row block 8][key block 8][lane 64][4]
  *                                 with lane 16 g + m holding S[16 rb + m][16 b + 4 g + j].
- *                                 In the affine-output form the combine then packs
- *                                 each later segment's start state to BF16 in place:
- *                                 blocks 2 kb and 2 kb + 1 as eight BF16 per lane over
- *                                 the FP32 fragment of block 2 kb.
+ *                                 Launch A writes segment 0's end state S_1 into slot
+ *                                 1 of the sequence, the zero-start end state Z_p of
+ *                                 segment p into slot p + 1 and (affine-output form)
+ *                                 the last segment's into the sequence's first slot.
+ *                                 The combine then writes each start state S_p over
+ *                                 slot p: in the affine-output form packed to BF16
+ *                                 (blocks 2 kb and 2 kb + 1 as eight BF16 per lane
+ *                                 over the FP32 fragment of block 2 kb). With the
+ *                                 carry-and-output launch (combine_workgroups == 0)
+ *                                 the slots are only read.
  *   scan_transition_offset        segmented form only: BF16 [H][S] slots of 128 x 128,
  *                                 each later segment's transition Phi, as fragments
  *                                 [key block 8][key group 4][lane 64][8] with lane
@@ -340,9 +347,14 @@ typedef struct kda_plan_info {
   size_t workspace_header_bytes;
   int64_t segment_chunks;          /* 0: serial form */
   int64_t segments_per_head_bound; /* scan slots per head */
-  int64_t combine_workgroups;
-  int64_t scan_c_workgroups;       /* the re-run launch, or the scan-output launch of the
-                                      affine-output form */
+  int64_t combine_workgroups;      /* 0 when the carry-and-output launch replaces it */
+  int64_t scan_c_workgroups;       /* the re-run launch, or the affine-output form's
+                                      scan-output launch, or its carry-and-output launch
+                                      (fixed layout, seven or more segments per
+                                      sequence: four 32-row blocks per later segment,
+                                      each forming its start state from S_1 and then
+                                      its output term; the last ones also the final
+                                      state) */
   size_t scan_state_offset;
   size_t scan_transition_offset;
   int32_t decode;                  /* 1: the token-loop kernel (1 <= T <= 8, see above) */

@@ -29,6 +29,9 @@ hipError_t launch_combine(const Params&, bool, hipStream_t) { return hipErrorInv
 hipError_t launch_scan_output(const Params&, int64_t, bool, hipStream_t) {
   return hipErrorInvalidValue;
 }
+hipError_t launch_carry_out(const Params&, int64_t, bool, bool, hipStream_t) {
+  return hipErrorInvalidValue;
+}
 hipError_t launch_decode(const Params&, bool, bool, hipStream_t) { return hipErrorInvalidValue; }
 }  // namespace kda
 

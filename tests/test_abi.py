@@ -229,11 +229,19 @@ def test_plan_segments_small_head_counts():
     assert p["segment_chunks"] == 47 and p["segments_per_head_bound"] == 11
     assert p["rows_per_workgroup"] == 64 and p["scan_affine_output"] == 1
     # Active row blocks of 64 rows only: segment 0's value rows, then value (Z) and
-    # transition (Phi) rows of segments 1 .. 10; the scan-output launch covers segments
-    # 1 .. 10 in groups of 4 chunks.
+    # transition (Phi) rows of segments 1 .. 10; with ten later segments the
+    # carry-and-output launch (four 32-row blocks per later segment) replaces the
+    # combine and the scan output.
     assert p["recurrence_workgroups"] == 6 * (2 + 4 * 10)
-    assert p["scan_c_workgroups"] == 6 * 10 * ((47 + 3) // 4)
-    assert p["combine_workgroups"] == 64  # 8 row blocks x 6 pairs, padded to 8 XCDs
+    assert p["scan_c_workgroups"] == 6 * 10 * 4
+    assert p["combine_workgroups"] == 0
+    # H = 12: P = (256 / 24 + 1) / 2 = 5 segments of 103 chunks, four later ones: the
+    # combine (8 row blocks x 12 pairs, padded to 8 XCDs) and the scan output (groups of
+    # 4 chunks).
+    p12 = kda.kda_prefill_plan(fake(H=12, T=8192), 256)
+    assert p12["segment_chunks"] == 103 and p12["scan_affine_output"] == 1
+    assert p12["combine_workgroups"] == 128
+    assert p12["scan_c_workgroups"] == 12 * 4 * ((103 + 3) // 4)
     records = 512 * 6 * kda.KDA_WS_RECORD
     assert p["scan_state_offset"] == records            # already 256-byte aligned
     slots = 6 * 11
@@ -252,6 +260,7 @@ def test_plan_segments_small_head_counts():
     assert c["scan_affine_output"] == 0 and c["scan_output_offset"] == 0
     assert c["recurrence_workgroups"] == 6 * (2 + 4 * 10)
     assert c["scan_c_workgroups"] == 6 * 11 * 2
+    assert c["combine_workgroups"] == 64  # 8 row blocks x 6 pairs, padded to 8 XCDs
     # 128-row workgroups when asked for: 2 P - 1 per pair, P = (256 / 6 + 1) / 2 = 21.
     w = kda.kda_prefill_plan(fake(H=6, T=8192, rows_per_workgroup=128), 256)
     assert w["segment_chunks"] == 25 and w["segments_per_head_bound"] == 21

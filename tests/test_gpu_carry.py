@@ -6,9 +6,10 @@ segments of 47 chunks with 64-row workgroups at H = 6, P = 3 of 171 chunks at H 
 (64-row) and at H = 48 (128-row). Under the benchmark recipe's strong decay only the
 first chunk of a segment feels its start state, so these runs use the weak_carry family,
 whose transition over one segment keeps every singular value above 0.1
-(tests/test_carry_family.py): the combine's S_p Phi_p + Z_p products, the scan output's
+(tests/test_carry_family.py): the S_p Phi_p + Z_p products that form each start state
+(at H = 6 inside the carry-and-output launch, at H = 24 and 48 in the combine), the
 (Qt Phi^T) S_p^T term at every chunk of a segment and the BF16 start states over ten
-combine steps all decide the result. Bound: max|err| / max|ref| <= 2e-2 for o and the
+steps all decide the result. Bound: max|err| / max|ref| <= 2e-2 for o and the
 final state, on every head at H = 6 and on sampled heads (each one complete over all
 tokens) at H = 24 and 48. The serial form (segment_chunks = -1) is checked on the same
 inputs.
@@ -57,6 +58,8 @@ def test_automatic_segments_carry(H, gscale, bscale, P, L, rows, heads):
     assert plan["segments_per_head_bound"] == P
     assert plan["rows_per_workgroup"] == rows
     assert plan["scan_affine_output"] == 1
+    # ten later segments: the carry-and-output launch; two: the combine and scan output
+    assert (plan["combine_workgroups"] == 0) == (P - 1 >= 6)
     o_ref, s_ref = run_oracle(x, heads=heads)
     hs = slice(None) if heads is None else heads
     for seg in (0, -1):  # automatic (segmented), then serial
