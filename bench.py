@@ -266,11 +266,13 @@ def time_config(x, steps, warmup, device, hip, **extra):
                               p90=round(us[min(steps - 1, int(0.9 * steps))], 2))
     del flush
     fix = lambda xs: [max(0.0, v - gap) for v in xs]
-    # The serial form has no combine or third launch: those phases hold only markers.
-    serial = statistics.median(comb) <= 1.5 * gap and statistics.median(rec_c) <= 1.5 * gap
+    # The serial form has no combine or third launch, and the carry-and-output form no
+    # combine: such phases hold only markers.
+    no_comb = statistics.median(comb) <= 1.5 * gap
+    serial = no_comb and statistics.median(rec_c) <= 1.5 * gap
     return dict(ms_per_step=total_ms / steps, wall_s=t_wall, prep_ms=fix(prep),
                 rec_ms=[max(0.0, v - 3 * gap) for v in rec],  # ev 1 -> 2 spans three records
-                rec_a_ms=fix(rec_a), combine_ms=[0.0] * steps if serial else fix(comb),
+                rec_a_ms=fix(rec_a), combine_ms=[0.0] * steps if no_comb else fix(comb),
                 rec_c_ms=[0.0] * steps if serial else fix(rec_c), event_gap_ms=gap,
                 serial=serial, per_call_us=per_call)
 
