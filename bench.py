@@ -246,15 +246,21 @@ def time_config(x, steps, warmup, device, hip, **extra):
     gap = statistics.median(hip.elapsed_ms(cal[2 * i], cal[2 * i + 1]) for i in range(steps))
     hip.destroy(cal)
 
-    # Per-call distribution, warm caches and with a 512 MB write between calls (evicts L2
-    # and the 256 MB MALL; untimed): each call between two events, one marker subtracted.
+    # Per-call distribution, each call between two events, one marker subtracted, with
+    # warm caches; "flushed": after a 512 MB write between calls (evicts L2 and the 256 MB
+    # MALL, and leaves them full of dirty lines that the call's own traffic writes back);
+    # "cold": after a 512 MB read between calls (evicts the inputs, leaves clean lines).
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+    flush_f = flush.view(torch.float32)
+    sink = torch.zeros(1, dtype=torch.float32, device=device)
     per_call = {}
-    for mode in ("warm", "flushed"):
+    for mode in ("warm", "flushed", "cold"):
         ev = hip.create(2 * steps)
         for i in range(steps):
             if mode == "flushed":
                 flush.fill_(i & 0xFF)
+            elif mode == "cold":
+                sink += flush_f.sum()
             hip.record(ev[2 * i], stream)
             call()
             hip.record(ev[2 * i + 1], stream)
@@ -264,7 +270,7 @@ def time_config(x, steps, warmup, device, hip, **extra):
         hip.destroy(ev)
         per_call[mode] = dict(median=round(statistics.median(us), 2), min=round(us[0], 2),
                               p90=round(us[min(steps - 1, int(0.9 * steps))], 2))
-    del flush
+    del flush, flush_f, sink
     fix = lambda xs: [max(0.0, v - gap) for v in xs]
     # The serial form has no combine or third launch, and the carry-and-output form no
     # combine: such phases hold only markers.
@@ -586,14 +592,13 @@ def main():
                 v["mfma_frac_of_measured_gemm"] = round(v["alg_flop"] / t / (gemm_tflops * 1e12), 5)
     if "config1" in per_config and "config3" in per_config:
         c1, c3 = per_config["config1"], per_config["config3"]
-        # t(H=96) / t(H=6) by step time, by warm per-call medians and by per-call medians
-        # with L2 and the 256 MB MALL flushed before each call (H=6's 63 MB of inputs
-        # fit in the MALL when warm).
+        # t(H=96) / t(H=6) by step time and by per-call medians: warm, flushed by a 512 MB
+        # write, and cold after a 512 MB read (H=6's 63 MB of inputs fit in the MALL when
+        # warm).
         per_config["head_scaling_t96_over_t6"] = round(c3["us"] / c1["us"], 3)
-        per_config["head_scaling_warm_per_call"] = round(
-            c3["per_call_us"]["warm"]["median"] / c1["per_call_us"]["warm"]["median"], 3)
-        per_config["head_scaling_flushed_per_call"] = round(
-            c3["per_call_us"]["flushed"]["median"] / c1["per_call_us"]["flushed"]["median"], 3)
+        for mode in ("warm", "flushed", "cold"):
+            per_config[f"head_scaling_{mode}_per_call"] = round(
+                c3["per_call_us"][mode]["median"] / c1["per_call_us"][mode]["median"], 3)
 
     cpu = None
     if not args.no_cpu_baseline:
