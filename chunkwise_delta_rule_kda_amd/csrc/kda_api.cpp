@@ -188,15 +188,18 @@ bool decode_form(const kda_prefill_args* a) {
 }
 
 // Rows per workgroup of the segmented form: the explicit choice, else 64, or a whole
-// head's 128 rows (eight compute waves, BF16 I/O) past 32 (sequence, head) pairs,
-// where 64-row segments no longer fit. A chunk takes ~1 us in a 128-row workgroup
-// under full load against ~0.55 us in a 64-row one, but a segment needs half the
-// workgroups: measured on T = 8192, H = 48 segments of 128 rows beat the serial form
-// (419 vs 432 us), while H = 6 loses with them (79.5 vs 73.5 us: the combine and the
-// scan output grow with the segment count).
+// head's 128 rows (eight compute waves, BF16 I/O) from kSegRows128MinPairs (sequence,
+// head) pairs on. A chunk takes ~0.95 us in a 128-row workgroup against ~0.53 us in a
+// 64-row one, but a segment needs half the workgroups, so there are about twice as many
+// segments. Measured per step at T = 8192, 64-row against 128-row segments: H = 8 77.7
+// vs 81.3 us, H = 9 87.0 vs 89.1, H = 10 104.4 vs 96.6, H = 11 103.3 vs 100.6, H = 12
+// 117.3 vs 110.7, H = 13 118.3 vs 113.1, H = 14 123.8 vs 126.9, H = 16 142.9 vs 142.4,
+// H = 18 153.8 vs 153.0, H = 20 190.2 vs 178.8, H = 24 205.8 vs 200.4, H = 32 258.7 vs
+// 251.7; from 33 pairs on 64-row segments no longer fit at all.
+constexpr int64_t kSegRows128MinPairs = 10;
 int segmented_rows(const kda_prefill_args* a) {
   if (a->rows_per_workgroup) return a->rows_per_workgroup;
-  return a->io_dtype == KDA_BF16 && a->N * a->H * 8 > kScanTargetCUs ? 128 : 64;
+  return a->io_dtype == KDA_BF16 && a->N * a->H >= kSegRows128MinPairs ? 128 : 64;
 }
 
 Plan make_plan(const kda_prefill_args* a) {

@@ -235,13 +235,21 @@ def test_plan_segments_small_head_counts():
     assert p["recurrence_workgroups"] == 6 * (2 + 4 * 10)
     assert p["scan_c_workgroups"] == 6 * 10 * 4
     assert p["combine_workgroups"] == 0
-    # H = 12: P = (256 / 24 + 1) / 2 = 5 segments of 103 chunks, four later ones: the
-    # combine (8 row blocks x 12 pairs, padded to 8 XCDs) and the scan output (groups of
-    # 4 chunks).
+    # From ten pairs on, 128-row segments: H = 12 gets P = (256 / 12 + 1) / 2 = 11
+    # segments of 47 chunks and the carry-and-output launch; H = 24 P = 5 segments of 103
+    # chunks, four later ones: the combine (8 row blocks x 24 pairs) and the scan output
+    # (groups of 4 chunks).
     p12 = kda.kda_prefill_plan(fake(H=12, T=8192), 256)
-    assert p12["segment_chunks"] == 103 and p12["scan_affine_output"] == 1
-    assert p12["combine_workgroups"] == 128
-    assert p12["scan_c_workgroups"] == 12 * 4 * ((103 + 3) // 4)
+    assert p12["segment_chunks"] == 47 and p12["rows_per_workgroup"] == 128
+    assert p12["recurrence_workgroups"] == 12 * (1 + 2 * 10)
+    assert p12["combine_workgroups"] == 0 and p12["scan_c_workgroups"] == 12 * 10 * 4
+    p24 = kda.kda_prefill_plan(fake(H=24, T=8192), 256)
+    assert p24["segment_chunks"] == 103 and p24["rows_per_workgroup"] == 128
+    assert p24["combine_workgroups"] == 192
+    assert p24["scan_c_workgroups"] == 24 * 4 * ((103 + 3) // 4)
+    # Nine pairs keep 64-row segments: P = (256 / 18 + 1) / 2 = 7.
+    p9 = kda.kda_prefill_plan(fake(H=9, T=8192), 256)
+    assert p9["rows_per_workgroup"] == 64 and p9["segment_chunks"] == 74
     records = 512 * 6 * kda.KDA_WS_RECORD
     assert p["scan_state_offset"] == records            # already 256-byte aligned
     slots = 6 * 11

@@ -7,7 +7,8 @@ recipe (g = -5 logistic(N(0,1))) Phi over a segment is below 1e-300, so a wrong 
 cannot show in any output. These pins show, with the oracle's identity-start, V = 0
 run, that ``kda_synth.stress("weak_carry", ...)`` at the scales the GPU carry tests use
 keeps every singular value of Phi above 0.1 over one automatic segment: 47 chunks (the
-automatic segment at H = 6, T = 8192) and 171 chunks (H = 24 and H = 48), and that the
+automatic segment at H = 6 and H = 12, T = 8192), 103 chunks (H = 24) and 171 chunks
+(H = 48), and that the
 start state then moves the last outputs of the segment by a visible fraction.
 """
 
@@ -20,7 +21,8 @@ from oracle import kda_recurrence_fp64
 D = 128
 
 
-@pytest.mark.parametrize("chunks,gscale,bscale", [(47, 2e-3, 0.2), (171, 5e-4, 0.05)])
+@pytest.mark.parametrize("chunks,gscale,bscale",
+                         [(47, 2e-3, 0.2), (103, 5e-4, 0.05), (171, 5e-4, 0.05)])
 def test_transition_over_one_segment_is_significant(chunks, gscale, bscale):
     x = kda_synth.stress("weak_carry", T=16 * chunks, H=1, gscale=gscale, bscale=bscale)
     eye = np.eye(D)[None, None]
