@@ -263,9 +263,10 @@ Plan make_plan(const kda_prefill_args* a) {
     pl.affine = a->checkpoint_every == 0;
     // Many segments per sequence (few heads): one carry-and-output launch in place of the
     // combine and the scan output. Measured at T = 8192 (BF16, per call): H = 6 (10 later
-    // segments) 65.1 against 69.1 us; H = 12 (4) 117.5 against 117.3 us; H = 24 and
-    // H = 48 (2) 207.0 against 204.6 us and 397 against 381 us, where the long segments
-    // stream their output terms faster through the scan output's many small workgroups.
+    // segments) 65.1 against 69.1 us; with 128-row segments H = 20 (5 later) 180.4 against
+    // 178.4 us, H = 24 (4) 204.4 against 200.5 us, H = 32 (3) 264.6 against 257.9 us,
+    // where the long segments stream their output terms faster through the scan output's
+    // many small workgroups.
     pl.carry = pl.affine && !a->cu_seqlens && pl.segs_per_seq - 1 >= kCarryMinLater;
     if (pl.affine) {
       pl.scan_q = round_up(end, 256);
