@@ -195,11 +195,16 @@ bool decode_form(const kda_prefill_args* a) {
 // vs 81.3 us, H = 9 87.0 vs 89.1, H = 10 104.4 vs 96.6, H = 11 103.3 vs 100.6, H = 12
 // 117.3 vs 110.7, H = 13 118.3 vs 113.1, H = 14 123.8 vs 126.9, H = 16 142.9 vs 142.4,
 // H = 18 153.8 vs 153.0, H = 20 190.2 vs 178.8, H = 24 205.8 vs 200.4, H = 32 258.7 vs
-// 251.7; from 33 pairs on 64-row segments no longer fit at all.
+// 251.7; from 33 pairs on 64-row segments no longer fit at all. The fused form keeps
+// 64-row segments up to 32 pairs: its chunk time grows more with the rows (the producer
+// waves share the CU with eight compute waves), H = 24 took 523 us per step in 128-row
+// segments against 357 us in 64-row ones.
 constexpr int64_t kSegRows128MinPairs = 10;
+constexpr int64_t kFusedSegRows128MinPairs = 33;
 int segmented_rows(const kda_prefill_args* a) {
   if (a->rows_per_workgroup) return a->rows_per_workgroup;
-  return a->io_dtype == KDA_BF16 && a->N * a->H >= kSegRows128MinPairs ? 128 : 64;
+  const int64_t from = fused_form(a) ? kFusedSegRows128MinPairs : kSegRows128MinPairs;
+  return a->io_dtype == KDA_BF16 && a->N * a->H >= from ? 128 : 64;
 }
 
 Plan make_plan(const kda_prefill_args* a) {

@@ -247,6 +247,12 @@ def test_plan_segments_small_head_counts():
     assert p24["segment_chunks"] == 103 and p24["rows_per_workgroup"] == 128
     assert p24["combine_workgroups"] == 192
     assert p24["scan_c_workgroups"] == 24 * 4 * ((103 + 3) // 4)
+    # The fused form keeps 64-row segments up to 32 pairs: H = 24, P = (256 / 48 + 1) / 2
+    # = 3 segments of 171 chunks; H = 48 takes 128 rows like the two-kernel form.
+    f24 = kda.kda_prefill_plan(fake(H=24, T=8192, fuse_prepare=1), 256)
+    assert f24["rows_per_workgroup"] == 64 and f24["segment_chunks"] == 171
+    f48 = kda.kda_prefill_plan(fake(H=48, T=8192, fuse_prepare=1), 256)
+    assert f48["rows_per_workgroup"] == 128 and f48["segment_chunks"] == 171
     # Nine pairs keep 64-row segments: P = (256 / 18 + 1) / 2 = 7.
     p9 = kda.kda_prefill_plan(fake(H=9, T=8192), 256)
     assert p9["rows_per_workgroup"] == 64 and p9["segment_chunks"] == 74
