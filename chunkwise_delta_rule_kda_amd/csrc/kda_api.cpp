@@ -144,8 +144,10 @@ int rows_per_wg(const kda_prefill_args* a, int num_cus) {
 }
 
 // Later segments per sequence from which the affine-output form uses the
-// carry-and-output launch (see make_plan).
+// carry-and-output launch, and from which it does so even when that launch needs more
+// than one workgroup per compute unit (see make_plan).
 constexpr int64_t kCarryMinLater = 6;
+constexpr int64_t kCarryMinLaterShared = 9;
 
 // Compute units the automatic segment rule is tuned for (MI355X). The rule must not
 // depend on the device so that the workspace size is a pure function of the arguments.
@@ -267,12 +269,20 @@ Plan make_plan(const kda_prefill_args* a) {
     end = pl.scan_phi + slots * kda::kD * kda::kD * 2;
     pl.affine = a->checkpoint_every == 0;
     // Many segments per sequence (few heads): one carry-and-output launch in place of the
-    // combine and the scan output. Measured at T = 8192 (BF16, per call): H = 6 (10 later
-    // segments) 65.1 against 69.1 us; with 128-row segments H = 20 (5 later) 180.4 against
-    // 178.4 us, H = 24 (4) 204.4 against 200.5 us, H = 32 (3) 264.6 against 257.9 us,
-    // where the long segments stream their output terms faster through the scan output's
-    // many small workgroups.
-    pl.carry = pl.affine && !a->cu_seqlens && pl.segs_per_seq - 1 >= kCarryMinLater;
+    // combine and the scan output. Measured per step at T = 8192 (BF16), carry against
+    // combine + scan output: 64-row segments H = 6 (10 later segments, 240 workgroups)
+    // 65.5 against 68.7 us, H = 8 (7, 224) 77.8 against 80.9; 128-row segments H = 10
+    // (12, 480) 96.2 against 96.7, H = 12 (10, 480) 109.5 against 110.5, H = 14 (8, 448)
+    // 127.1 against 125.6, H = 16 (7, 448) 140.6 against 139.0, H = 20 (5) 180.4 against
+    // 178.4, H = 24 (4) 204.4 against 200.5, H = 32 (3) 264.6 against 257.9. With two of
+    // its workgroups per compute unit the chains' operand streams share the unit, and
+    // with few long segments the scan output's many small workgroups stream the output
+    // terms faster.
+    {
+      const int64_t later = pl.segs_per_seq - 1;
+      pl.carry = pl.affine && !a->cu_seqlens && later >= kCarryMinLater &&
+                 (a->H * a->N * later * 4 <= kScanTargetCUs || later >= kCarryMinLaterShared);
+    }
     if (pl.affine) {
       pl.scan_q = round_up(end, 256);
       end = pl.scan_q + static_cast<size_t>(pl.max_chunks) * static_cast<size_t>(a->H) * 2048 *

@@ -351,7 +351,8 @@ typedef struct kda_plan_info {
   int64_t scan_c_workgroups;       /* the re-run launch, or the affine-output form's
                                       scan-output launch, or its carry-and-output launch
                                       (fixed layout, seven or more segments per
-                                      sequence: four 32-row blocks per later segment,
+                                      sequence, ten or more when H * N * (P - 1) * 4
+                                      exceeds 256: four 32-row blocks per later segment,
                                       each forming its start state from S_1 and then
                                       its output term; the last ones also the final
                                       state) */

@@ -247,6 +247,13 @@ def test_plan_segments_small_head_counts():
     assert p24["segment_chunks"] == 103 and p24["rows_per_workgroup"] == 128
     assert p24["combine_workgroups"] == 192
     assert p24["scan_c_workgroups"] == 24 * 4 * ((103 + 3) // 4)
+    # The carry-and-output launch needs six later segments, and nine when its grid
+    # (H x later x 4 workgroups) exceeds 256: H = 8 (64-row, 7 later, 224) and H = 13
+    # (128-row, 9 later, 468) take it, H = 14 (8 later, 448) keeps the combine.
+    for H, later, carry in ((8, 7, True), (13, 9, True), (14, 8, False), (18, 6, False)):
+        ph = kda.kda_prefill_plan(fake(H=H, T=8192), 256)
+        assert -(-512 // ph["segment_chunks"]) - 1 == later, H
+        assert (ph["combine_workgroups"] == 0) == carry, H
     # The fused form keeps 64-row segments up to 32 pairs: H = 24, P = (256 / 48 + 1) / 2
     # = 3 segments of 171 chunks; H = 48 takes 128 rows like the two-kernel form.
     f24 = kda.kda_prefill_plan(fake(H=24, T=8192, fuse_prepare=1), 256)
