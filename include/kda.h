@@ -132,8 +132,8 @@ typedef struct kda_prefill_args {
      compute wave owns 16 rows). 0 = automatic: in the serial form the smallest of 16,
      32 and 64 that keeps N * H * 128 / rows within the device's compute units, else
      128 for BF16 I/O (64 for FP32); in the segmented form 64, or 128 for BF16 I/O
-     past N * H = 32. 16/32/64/128 force it. For a given segment_chunks, results are
-     bitwise identical for every choice. */
+     from N * H = 10 on (past N * H = 32 in the fused form). 16/32/64/128 force it.
+     For a given segment_chunks, results are bitwise identical for every choice. */
   int32_t rows_per_workgroup;
 
   /* Time segments of the recurrence. The chunk-to-chunk carry is affine in the state,
@@ -144,14 +144,17 @@ typedef struct kda_prefill_args {
      also writes each later segment's zero-start output into o and the output of its
      transition run (Qt Phi^T per chunk) into the workspace, the combine's last step
      writes the final state, and a parallel pass adds (Qt Phi^T) S_p^T to o: a critical
-     path of about one segment plus the combine. With checkpoints every later segment
+     path of about one segment plus the combine. With many segments (fixed layout) one
+     carry-and-output launch replaces the combine and that pass: each later segment's
+     workgroups form their own start state by the chain of transitions and then add its
+     output term (see scan_c_workgroups). With checkpoints every later segment
      is instead re-run from its true start (the states inside it are needed): about two
      segments. Either way about twice or three times the recurrence work buys the
      shorter path, which pays off when few (sequence, head) pairs leave compute units
      idle. 0 = automatic: P segments (of at least 16 chunks) such that the first pass
-     has about one workgroup per compute unit of a 256-CU device, with 64-row
-     workgroups (128-row ones for BF16 I/O past N * H = 32) unless rows_per_workgroup
-     says otherwise, taken when P >= 3, or P >= 2 with N * H <= 32; negative = never
+     has about one workgroup per compute unit of a 256-CU device, with the segmented
+     form's automatic rows (see rows_per_workgroup) unless rows_per_workgroup says
+     otherwise, taken when P >= 3, or P >= 2 with N * H <= 32; negative = never
      (one serial run per sequence); positive = this many chunks per segment. Results
      differ from the serial form only by rounding. */
   int32_t segment_chunks;

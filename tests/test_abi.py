@@ -287,9 +287,9 @@ def test_plan_segments_small_head_counts():
     assert w["segment_chunks"] == 25 and w["segments_per_head_bound"] == 21
     assert w["rows_per_workgroup"] == 128 and w["waves_per_workgroup"] == 8 + 4
     assert w["recurrence_workgroups"] == 6 * (1 + 2 * 20)
-    # Past 32 pairs (BF16 I/O) the automatic segments use 128-row workgroups and need
-    # three segments: H = 48 (P = 3) is segmented, H = 64 (P = 2) and H = 96 are not;
-    # with FP32 I/O H = 48 stays serial.
+    # Past 32 pairs (BF16 I/O, 128-row workgroups as from 10 pairs on) the automatic
+    # segments need three segments: H = 48 (P = 3) is segmented, H = 64 (P = 2) and
+    # H = 96 are not; with FP32 I/O (64-row) H = 48 stays serial.
     h48 = kda.kda_prefill_plan(fake(H=48, T=8192), 256)
     assert h48["segment_chunks"] == 171 and h48["rows_per_workgroup"] == 128
     assert h48["recurrence_workgroups"] == 48 * 5
