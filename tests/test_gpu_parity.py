@@ -65,6 +65,20 @@ def test_batch_fixed_layout():
     check(kda_synth.config(2, T=48, H=2, B=3), "batch3")
 
 
+def test_heads_fast_preparation_grid_end_to_end():
+    # H = 32 (the preparation grid's heads-fastest order) with packed sequences, an empty
+    # one and a ragged last grid row; the oracle runs three heads in full.
+    x = kda_synth.config(4, H=32, lengths=[700, 0, 33, 513, 250])
+    heads = [0, 17, 31]
+    print(f"[case] heads-fast grid: N={x.N} T={x.T} H={x.H} heads={heads}", flush=True)
+    o, s, _ = run_gpu(x)
+    o_ref, s_ref = run_oracle(x, heads=heads)
+    eo, es = rel_err(o[:, :, heads], o_ref), rel_err(s[:, heads], s_ref)
+    print(f"[case] heads-fast grid: o err {eo:.3e} state err {es:.3e}", flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(s))
+    assert eo <= TOL and es <= TOL
+
+
 # ---- stress inputs (carry and inverse matter) ----------------------------------------
 @pytest.mark.parametrize("family,T", [("weak_decay", 256), ("correlated", 128),
                                       ("floor", 128)])
